@@ -1,0 +1,265 @@
+/*
+ * gcache.h -- C ABI of libgcache.so: quantized paged KV-cache write and
+ * gather-upconvert for AMD Instinct MI355X (gfx950).
+ *
+ * Operations (sources are prhub.com.cn digests of three vLLM pull requests):
+ *   [PR51724] "W4A16 DSA" -- nvfp4_ds_mla cache: the write
+ *             concat_and_cache_nvfp4_ds_mla and the prefill gather
+ *             cp_gather_and_upconvert_nvfp4_kv_cache ("Implementation
+ *             breakdown" items 2-4, "Key source excerpts").
+ *   [PR48642] "Sparse MLA: enable fp8_ds_mla dense prefill" -- the fp8_ds_mla
+ *             gather cp_gather_and_upconvert_fp8_kv_cache with seq_starts
+ *             ("Implementation breakdown" items 2 and 4, the
+ *             _compute_prefill_context excerpt).
+ *   [PR37332] NVFP4 per-head K/V cache for reshape_and_cache_flash
+ *             ("Motivation", "Implementation breakdown" items 1 and 4,
+ *             "Key source excerpts").
+ *
+ * Conventions shared by every entry point
+ * ----------------------------------------
+ *  - Every array argument is a DEVICE pointer owned by the caller (the one
+ *    exception, the per-head layout struct, is a host pointer read during the
+ *    call).  The library never allocates, frees or synchronizes: each call
+ *    validates its arguments on the host and enqueues kernels on `stream`
+ *    (which must belong to the current device).
+ *  - bf16 data is IEEE bfloat16 bits; e4m3 is the OCP E4M3FN format (no
+ *    infinities, 0x7F/0xFF NaN, max 448); e2m1 is OCP MX E2M1.
+ *  - Strides are in ELEMENTS of the array they describe for bf16 arrays and in
+ *    BYTES for the uint8 caches.  Offsets into a cache are 64-bit.
+ *  - Return value: GCACHE_OK, or a negative gcache_status when an argument is
+ *    rejected (nothing is launched then), when the current device is not a
+ *    gfx950 GPU (GCACHE_ERR_UNSUPPORTED) or when the launch itself fails.
+ *    Faults inside a kernel surface at the caller's next synchronization.
+ *  - Not checked (caller contract, as in the pages' kernels): slot and block
+ *    ids lie inside the cache, slots are distinct, workspace_starts is
+ *    non-decreasing with workspace_starts[0] == 0, and every block-table entry
+ *    a row reads is valid.  Inputs are finite.
+ *  - Calls are asynchronous and stream-ordered; two calls that write the same
+ *    cache bytes on different streams race.
+ *
+ * Numerics (bit-exact against the CPU reference in oracle/):
+ *  - NVFP4 block of 16 values x: sf = e4m3_rn_sat(amax(|x|) / 6) in binary32,
+ *    inv = 1 / dec(sf) (0 when sf decodes to 0), code = e2m1_rn_sat(x * inv).
+ *    The even element of a pair is the low nibble.
+ *  - e4m3 RoPE: e4m3_rn_sat(r), no scale.
+ *  - NVFP4 dequant: bf16(e2m1 * e4m3) -- exact, no rounding.
+ */
+#ifndef GCACHE_H
+#define GCACHE_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GCACHE_OK = 0,
+    GCACHE_ERR_NULL = -1,         /* a required pointer is NULL */
+    GCACHE_ERR_SHAPE = -2,        /* a size or stride is out of range */
+    GCACHE_ERR_ALIGN = -3,        /* a base or stride breaks the 16-byte vector alignment */
+    GCACHE_ERR_UNSUPPORTED = -4,  /* current device is not gfx950, or a shape the kernels do not cover */
+    GCACHE_ERR_DEVICE = -5,       /* a HIP runtime query failed */
+    GCACHE_ERR_LAUNCH = -6        /* the kernel launch failed */
+} gcache_status;
+
+typedef enum {
+    GCACHE_NVFP4_DS_MLA = 0,      /* 352-byte entry */
+    GCACHE_FP8_DS_MLA = 1         /* 656-byte entry */
+} gcache_format;
+
+/* Bytes per token of a DS-MLA cache entry: 352 (nvfp4_ds_mla) or 656
+ * (fp8_ds_mla) -- [PR51724] "Implementation breakdown" item 2.  Returns -1
+ * for an unknown format. */
+int64_t gcache_entry_bytes(gcache_format format);
+
+/* Packed last dimension of the per-head NVFP4 cache: head_size/2 data bytes
+ * plus head_size/16 e4m3 scale bytes -- [PR37332] "Key source excerpts"
+ * (get_kv_cache_shape).  Returns -1 unless head_size is a positive multiple
+ * of 16. */
+int32_t gcache_nvfp4_full_dim(int32_t head_size);
+
+/* Human-readable name of a gcache_status value (static storage). */
+const char* gcache_status_string(int status);
+
+/*
+ * nvfp4_ds_mla write -- [PR51724] "Implementation breakdown" item 3 and the
+ * write-kernel excerpt in "Key source excerpts".
+ *
+ * For every token t with slot = slot_mapping[t] >= 0, quantizes the 512 NoPE
+ * values kv_c[t, 0:512] and the 64 RoPE values k_pe[t, 0:64] into the
+ * 352-byte entry at
+ *     kv_cache + (slot / block_size) * block_stride + (slot % block_size) * entry_stride
+ * laid out as [0,256) e2m1 NoPE (16 values -> 8 bytes at 8*j for block j),
+ * [256,320) e4m3 RoPE, [320,352) the 32 e4m3 NoPE block scales (scale j at
+ * byte 320 + j).  Tokens with slot < 0 are padding: nothing is read or
+ * written for them.  Bytes outside the written entries are never touched.
+ *
+ *  kv_c         bf16 [num_tokens, >=512], row stride kv_c_stride elements
+ *  k_pe         bf16 [num_tokens, >=64],  row stride k_pe_stride elements
+ *  kv_cache     uint8, num_blocks blocks of block_stride bytes
+ *  slot_mapping int64 [num_tokens]
+ * Requirements: num_tokens >= 0 (0 is a no-op), block_size > 0,
+ * entry_stride >= 352, block_stride >= block_size * entry_stride;
+ * kv_c and k_pe 16-byte aligned with strides that are multiples of 8
+ * elements; kv_cache, block_stride and entry_stride multiples of 16 bytes.
+ */
+int gcache_cache_write_nvfp4_ds_mla(const void* kv_c, const void* k_pe, void* kv_cache,
+                                    const int64_t* slot_mapping, int64_t num_tokens,
+                                    int64_t kv_c_stride, int64_t k_pe_stride,
+                                    int64_t num_blocks, int32_t block_size,
+                                    int64_t block_stride, int64_t entry_stride,
+                                    hipStream_t stream);
+
+/*
+ * fp8_ds_mla write -- the 656-byte entry of [PR51724] "Implementation
+ * breakdown" item 2 (the pages fix only its size; the layout here is this
+ * library's reading): [0,512) e4m3 NoPE codes, [512,528) four little-endian
+ * fp32 scales, one per 128 values, scale = amax / 448 and code =
+ * e4m3_rn_sat(x * (1 / scale)) (0 when scale is 0), [528,656) the 64 RoPE
+ * values copied as bf16.  Same arguments and requirements as the nvfp4
+ * write with entry_stride >= 656 (a multiple of 16).
+ * Contract: a 128-value group whose amax is below 448 * 2^-126 (its
+ * reciprocal scale overflows) gives unspecified codes.
+ */
+int gcache_cache_write_fp8_ds_mla(const void* kv_c, const void* k_pe, void* kv_cache,
+                                  const int64_t* slot_mapping, int64_t num_tokens,
+                                  int64_t kv_c_stride, int64_t k_pe_stride,
+                                  int64_t num_blocks, int32_t block_size,
+                                  int64_t block_stride, int64_t entry_stride,
+                                  hipStream_t stream);
+
+/*
+ * nvfp4_ds_mla gather-upconvert -- [PR51724] prefill gather excerpt
+ * ("Key source excerpts"), with the seq_starts walk of [PR48642]
+ * ("Implementation breakdown" item 2).
+ *
+ * Workspace row r (0 <= r < total_tokens) belongs to request b = the largest
+ * b < batch_size with workspace_starts[b] <= r (request b owns rows
+ * [ws[b], ws[b+1]); the last request ends at total_tokens, so trailing and
+ * empty requests are allowed).  It reads logical position
+ *     p = seq_starts[b] + (r - workspace_starts[b])      (seq_starts NULL: 0)
+ * of the request, i.e. the entry at offset p % block_size of cache block
+ * block_table[b * block_table_stride + p / block_size], and writes
+ *     dst[r, 0:512]   = bf16(e2m1 * e4m3 block scale)   (exact)
+ *     dst[r, 512:576] = bf16(e4m3 RoPE)                  (exact)
+ *
+ *  src_cache        uint8 cache written by gcache_cache_write_nvfp4_ds_mla
+ *  dst              bf16 [total_tokens, >=576], row stride dst_stride elements
+ *  block_table      int32 [batch_size, block_table_stride]
+ *  workspace_starts int32 [batch_size]; seq_starts int32 [batch_size] or NULL
+ * Requirements: total_tokens >= 0 (0 is a no-op), batch_size > 0 when
+ * total_tokens > 0, dst 16-byte aligned and dst_stride a multiple of 8,
+ * src_cache, block_stride and entry_stride multiples of 16 bytes,
+ * entry_stride >= 352.
+ */
+int gcache_cache_gather_upconvert_nvfp4_ds_mla(const void* src_cache, void* dst,
+                                               int64_t total_tokens, int64_t dst_stride,
+                                               const int32_t* block_table,
+                                               int64_t block_table_stride,
+                                               const int32_t* workspace_starts,
+                                               const int32_t* seq_starts, int32_t batch_size,
+                                               int64_t num_blocks, int32_t block_size,
+                                               int64_t block_stride, int64_t entry_stride,
+                                               hipStream_t stream);
+
+/*
+ * fp8_ds_mla gather-upconvert -- [PR48642] "Implementation breakdown" items
+ * 2 and 4: cp_gather_and_upconvert_fp8_kv_cache with seq_starts (seq_lens
+ * removed), BF16 workspace.  Same walk and arguments as the nvfp4 gather;
+ *     dst[r, i]       = bf16_rne(binary32(e4m3(code i) * scale[i / 128]))
+ *     dst[r, 512:576] = the stored bf16 RoPE values
+ * Requirements as for the nvfp4 gather with entry_stride >= 656.
+ */
+int gcache_cache_gather_upconvert_fp8_ds_mla(const void* src_cache, void* dst,
+                                             int64_t total_tokens, int64_t dst_stride,
+                                             const int32_t* block_table,
+                                             int64_t block_table_stride,
+                                             const int32_t* workspace_starts,
+                                             const int32_t* seq_starts, int32_t batch_size,
+                                             int64_t num_blocks, int32_t block_size,
+                                             int64_t block_stride, int64_t entry_stride,
+                                             hipStream_t stream);
+
+/*
+ * Per-head NVFP4 K/V cache geometry, in BYTES from the start of the cache
+ * ([PR37332] "Key source excerpts": allocation (num_blocks, 2, block_size,
+ * num_heads, full_dim), split views into data and scale parts that keep the
+ * NHD or HND order).  For block blk, side c (0 = K, 1 = V), token offset o
+ * and head h:
+ *   data  (head_size/2 bytes):  blk*block_stride + c*side_stride + data_offset
+ *                               + o*data_token_stride + h*data_head_stride
+ *   scale (head_size/16 bytes): blk*block_stride + c*side_stride + scale_offset
+ *                               + o*scale_token_stride + h*scale_head_stride
+ */
+typedef struct {
+    int64_t data_offset, data_token_stride, data_head_stride;
+    int64_t scale_offset, scale_token_stride, scale_head_stride;
+    int64_t side_stride, block_stride;
+} gcache_nvfp4_kv_layout;
+
+/* Fills *out with the split layout of [PR37332] ("Motivation": K data, K
+ * scales, V data, V scales, each contiguous): every side of a block is all
+ * data rows [block_size][num_heads][head_size/2] followed by all scale rows
+ * [block_size][num_heads][head_size/16]; block_stride = 2 * block_size *
+ * num_heads * full_dim.  Returns GCACHE_ERR_SHAPE for bad sizes. */
+int gcache_nvfp4_kv_split_layout(int32_t block_size, int32_t num_heads, int32_t head_size,
+                                 gcache_nvfp4_kv_layout* out);
+
+/*
+ * Per-head NVFP4 write (reshape_and_cache_nvfp4) -- [PR37332]
+ * "Implementation breakdown" item 4.
+ *
+ * For every token t with slot >= 0 (block slot / block_size, offset
+ * slot % block_size), side c in {K, V} with per-tensor scale gs (*k_scale or
+ * *v_scale, device fp32 scalars > 0), head h and 16-value block j:
+ *     sf = e4m3_rn_sat((amax / 6) / gs);  e = dec(sf) * gs;
+ *     inv = 1 / e (0 when e is 0);        code = e2m1_rn_sat(x * inv)
+ * The head's head_size/2 data bytes and head_size/16 scale bytes go to the
+ * layout addresses above.
+ *
+ *  key, value  bf16 [num_tokens, num_heads, head_size] with the given token
+ *              and head strides (elements; multiples of 8, bases 16-byte aligned)
+ *  kv_cache    uint8 cache; layout: host pointer (data and scale offsets and
+ *              strides multiples of 8 and 1 bytes respectively)
+ * Requirements: head_size a positive multiple of 16 (at most 1024),
+ * num_heads > 0, block_size > 0.
+ */
+int gcache_reshape_and_cache_nvfp4(const void* key, const void* value,
+                                   int64_t key_token_stride, int64_t key_head_stride,
+                                   int64_t value_token_stride, int64_t value_head_stride,
+                                   void* kv_cache, const int64_t* slot_mapping,
+                                   int64_t num_tokens, int32_t num_heads, int32_t head_size,
+                                   int64_t num_blocks, int32_t block_size,
+                                   const gcache_nvfp4_kv_layout* layout,
+                                   const float* k_scale, const float* v_scale,
+                                   hipStream_t stream);
+
+/*
+ * Per-head NVFP4 gather-upconvert -- the read side of the [PR37332] layout
+ * (the pages dequantize it in test helpers, "Implementation breakdown"
+ * item 5).  Same walk as the DS-MLA gathers; for every workspace row r and
+ * side c:
+ *     out[r, h, i] = bf16_rne(binary32((e2m1 * e4m3 block scale) * gs))
+ *  key_out, value_out  bf16 [total_tokens, num_heads, head_size] with token
+ *                      and head strides (elements; multiples of 8, bases
+ *                      16-byte aligned)
+ * Other arguments as in gcache_reshape_and_cache_nvfp4 and the DS-MLA gather.
+ */
+int gcache_gather_upconvert_nvfp4_kv(const void* kv_cache, void* key_out, void* value_out,
+                                     int64_t total_tokens,
+                                     int64_t key_token_stride, int64_t key_head_stride,
+                                     int64_t value_token_stride, int64_t value_head_stride,
+                                     const int32_t* block_table, int64_t block_table_stride,
+                                     const int32_t* workspace_starts, const int32_t* seq_starts,
+                                     int32_t batch_size, int32_t num_heads, int32_t head_size,
+                                     int64_t num_blocks, int32_t block_size,
+                                     const gcache_nvfp4_kv_layout* layout,
+                                     const float* k_scale, const float* v_scale,
+                                     hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GCACHE_H */
