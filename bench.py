@@ -1,0 +1,321 @@
+"""Benchmark of the quantized paged KV-cache hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+One step = one pass of every operation of the path, each over its full
+synthetic workload, inputs resident in HBM:
+
+  1. nvfp4_ds_mla write      524288 tokens into 8192 x 64 x 352 B (pre-fill)
+  2. fp8_ds_mla write        1048576 tokens into 16384 x 64 x 656 B (pre-fill)
+  3. nvfp4_ds_mla gather     16 requests, L ~ U[1024, 32768], from seq_starts
+  4. per-head NVFP4 write    8192 tokens x 8 heads x 128 (1% padding)
+  5. fp8_ds_mla gather       32 requests, L ~ U[512, 16384], from seq_starts
+  6. per-head NVFP4 gather   every written token back to bf16 K and V
+
+(writes and the gathers over their caches are interleaved so that a gather
+does not find its freshly written cache in the 256 MB last-level cache).
+
+Prints ONE JSON line: the whole step's effective HBM throughput (algorithmic
+bytes / wall time per step), per-kernel HIP-event durations and GB/s, the
+roofline of the dominant kernel and the CPU oracle's throughput on a bounded
+sample of the same workloads.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak, GB/s
+NV, F8 = 352, 656
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=15.0,
+                    help="approximate CPU seconds for the oracle baseline sample")
+    ap.add_argument("--cold", action="store_true",
+                    help="also time every kernel once per run after evicting the caches")
+    ap.add_argument("--only", default=None, help="comma list of op names to run (profiling aid)")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# Workloads and their algorithmic bytes
+# ---------------------------------------------------------------------------
+def build_workloads():
+    import synth
+    w3 = synth.config3_prefill()
+    g3 = synth.config3_gather()
+    w4 = synth.config4_prefill()
+    g4 = synth.config4_gather()
+    w5, g5 = synth.config5()
+    return w3, g3, w4, g4, w5, g5
+
+
+def ds_write_bytes(w, entry):
+    valid = int((w.slot_mapping >= 0).sum())
+    return valid * (512 * 2 + 64 * 2 + entry) + w.num_tokens * 8
+
+
+def ds_gather_bytes(g, entry):
+    return g.total_tokens * (entry + 576 * 2)
+
+
+def kv_write_bytes(w):
+    T, H, hs = w.key.shape
+    valid = int((w.slot_mapping >= 0).sum())
+    return valid * 2 * H * (hs * 2 + hs // 2 + hs // 16) + T * 8
+
+
+def kv_gather_bytes(g, H, hs):
+    return g.total_tokens * 2 * H * (hs * 2 + hs // 2 + hs // 16)
+
+
+# ---------------------------------------------------------------------------
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
+              "(the path is token-parallel; see the design notes for how it shards).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import gather_concat_cache_amd as gc
+
+    def dev_bf16(a):          # bf16 bits (uint16) -> device bfloat16, bit for bit
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+    def dev_arr(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    torch.cuda.init()
+    dname = torch.cuda.get_device_name(0)
+    t0 = time.time()
+    w3, g3, w4, g4, w5, g5 = build_workloads()
+    gen_s = time.time() - t0
+
+    H, hs = w5.key.shape[1], w5.key.shape[2]
+    fd = hs // 2 + hs // 16
+    # ---- device-resident inputs and outputs
+    d = {}
+    d["kv3"], d["pe3"], d["sl3"] = dev_bf16(w3.kv_c), dev_bf16(w3.k_pe), dev_arr(w3.slot_mapping)
+    d["cache3"] = torch.zeros((w3.num_blocks, w3.block_size, NV), dtype=torch.uint8, device="cuda")
+    d["bt3"], d["ws3"], d["ss3"] = dev_arr(g3.block_table), dev_arr(g3.workspace_starts), dev_arr(g3.seq_starts)
+    d["dst3"] = torch.empty((g3.total_tokens, 576), dtype=torch.bfloat16, device="cuda")
+    d["kv4"], d["pe4"], d["sl4"] = dev_bf16(w4.kv_c), dev_bf16(w4.k_pe), dev_arr(w4.slot_mapping)
+    d["cache4"] = torch.zeros((w4.num_blocks, w4.block_size, F8), dtype=torch.uint8, device="cuda")
+    d["bt4"], d["ws4"], d["ss4"] = dev_arr(g4.block_table), dev_arr(g4.workspace_starts), dev_arr(g4.seq_starts)
+    d["dst4"] = torch.empty((g4.total_tokens, 576), dtype=torch.bfloat16, device="cuda")
+    d["k5"], d["v5"], d["sl5"] = dev_bf16(w5.key), dev_bf16(w5.value), dev_arr(w5.slot_mapping)
+    d["cache5"] = torch.zeros((w5.num_blocks, 2, w5.block_size, H, fd), dtype=torch.uint8, device="cuda")
+    d["ks5"] = torch.tensor([w5.k_scale], dtype=torch.float32, device="cuda")
+    d["vs5"] = torch.tensor([w5.v_scale], dtype=torch.float32, device="cuda")
+    d["bt5"], d["ws5"], d["ss5"] = dev_arr(g5.block_table), dev_arr(g5.workspace_starts), dev_arr(g5.seq_starts)
+    d["ko5"] = torch.empty((g5.total_tokens, H, hs), dtype=torch.bfloat16, device="cuda")
+    d["vo5"] = torch.empty((g5.total_tokens, H, hs), dtype=torch.bfloat16, device="cuda")
+
+    ops = [
+        ("nvfp4_ds_mla_write", ds_write_bytes(w3, NV), w3.num_tokens,
+         lambda: gc.cache_write_nvfp4_ds_mla(d["kv3"], d["pe3"], d["cache3"], d["sl3"])),
+        ("fp8_ds_mla_write", ds_write_bytes(w4, F8), w4.num_tokens,
+         lambda: gc.cache_write_fp8_ds_mla(d["kv4"], d["pe4"], d["cache4"], d["sl4"])),
+        ("nvfp4_ds_mla_gather", ds_gather_bytes(g3, NV), g3.total_tokens,
+         lambda: gc.cache_gather_upconvert_nvfp4_ds_mla(d["cache3"], d["dst3"], d["bt3"], d["ws3"], d["ss3"])),
+        ("nvfp4_kv_write", kv_write_bytes(w5), w5.slot_mapping.shape[0],
+         lambda: gc.reshape_and_cache_nvfp4(d["k5"], d["v5"], d["cache5"], d["sl5"], d["ks5"], d["vs5"])),
+        ("fp8_ds_mla_gather", ds_gather_bytes(g4, F8), g4.total_tokens,
+         lambda: gc.cache_gather_upconvert_fp8_ds_mla(d["cache4"], d["dst4"], d["bt4"], d["ws4"], d["ss4"])),
+        ("nvfp4_kv_gather", kv_gather_bytes(g5, H, hs), g5.total_tokens,
+         lambda: gc.gather_upconvert_nvfp4_kv(d["cache5"], d["ko5"], d["vo5"], d["bt5"], d["ws5"], d["ks5"],
+                                              d["vs5"], seq_starts=d["ss5"])),
+    ]
+    if args.only:
+        keep = set(args.only.split(","))
+        ops = [o for o in ops if o[0] in keep]
+    step_bytes = sum(o[1] for o in ops)
+
+    def step(events=None):
+        for i, (_, _, _, fn) in enumerate(ops):
+            if events is not None:
+                events[i][0].record()
+            fn()
+            if events is not None:
+                events[i][1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # ---- timed region: K steps, HIP events around every kernel on the launch stream
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in ops]
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for k in range(args.steps):
+        step(ev[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_per_step = wall * 1e3 / args.steps
+    kern_ms = {name: float(np.mean([ev[k][i][0].elapsed_time(ev[k][i][1]) for k in range(args.steps)]))
+               for i, (name, _, _, _) in enumerate(ops)}
+
+    kernels = {}
+    for name, nbytes, units, _ in ops:
+        ms = kern_ms[name]
+        kernels[name] = {"ms": round(ms, 5), "bytes": nbytes, "units": units,
+                         "GB_per_s": round(nbytes / (ms * 1e6), 1),
+                         "frac_of_hbm_peak": round(nbytes / (ms * 1e6) / HBM_PEAK_GBS, 4)}
+
+    cold = None
+    if args.cold:
+        cold = measure_cold(torch, ops)
+
+    dom = max(ops, key=lambda o: kern_ms[o[0]])
+    achieved = dom[1] / (kern_ms[dom[0]] * 1e6)
+    roofline = {"kernel": dom[0], "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic_for(dom[0])}
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_budget_s, w3, g3, w4, g4, w5, g5)
+
+    value = step_bytes / (ms_per_step * 1e6)
+    out = {
+        "metric": "effective HBM GB/s (% of peak) for NVFP4 DS-MLA cache write and gather-upconvert",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16->e2m1/e4m3 (u8) and back", "data": "synthetic (seeded, see synth/)",
+        "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "config": {"workload": "prefill-context pass: nvfp4_ds_mla write 524288 tok + gather 16 req "
+                               f"({g3.total_tokens} rows); fp8_ds_mla write 1048576 tok + gather 32 req "
+                               f"({g4.total_tokens} rows); per-head nvfp4 write 8192 tok x 8 heads x 128 "
+                               f"+ gather {g5.total_tokens} rows",
+                   "step_bytes": step_bytes, "ops": [o[0] for o in ops], "device": dname},
+        "kernels": kernels,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "input_generation_s": round(gen_s, 2),
+    }
+    if cold is not None:
+        out["kernels_cold"] = cold
+    print(json.dumps(out), flush=True)
+
+
+def measure_cold(torch, ops, reps=5):
+    """Each kernel alone after writing a 2 GiB buffer (evicts L2 and the
+    256 MB MALL); median over reps."""
+    flush = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
+    res = {}
+    for name, nbytes, _, fn in ops:
+        t = []
+        for _ in range(reps):
+            flush.zero_()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            t.append(a.elapsed_time(b))
+        ms = float(np.median(t))
+        res[name] = {"ms": round(ms, 5), "GB_per_s": round(nbytes / (ms * 1e6), 1)}
+    del flush
+    return res
+
+
+def traffic_for(kernel):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, when
+    it was taken on the current kernel source (else null)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            t = json.load(f)
+        from gather_concat_cache_amd.build import source_digest
+        if t.get("source_digest") != source_digest():
+            return None
+        return t["kernels"].get(kernel, {}).get("hbm_bytes_per_launch")
+    except Exception:
+        return None
+
+
+# ---------------------------------------------------------------------------
+def cpu_baseline(budget_s, w3, g3, w4, g4, w5, g5):
+    """The oracle, as it stands, on a bounded sample of each workload, one
+    host thread.  Write samples: the first n tokens of each pre-fill; gather
+    samples: the first rows of each gather, reading a cache that holds the
+    oracle's own output for the sampled tokens (other entries zero; the
+    decode cost does not depend on the bytes).  GB/s from the same
+    algorithmic byte counts as the GPU figures."""
+    import oracle
+    frac = budget_s / 15.0
+    n3, n4, n5 = int(16384 * frac), int(16384 * frac), int(1024 * frac)
+    r3, r4 = int(16384 * frac), int(16384 * frac)
+    res, tot_bytes, tot_s = {}, 0, 0.0
+
+    def timed(name, nbytes, fn):
+        nonlocal tot_bytes, tot_s
+        t = time.perf_counter()
+        fn()
+        s = time.perf_counter() - t
+        res[name] = {"s": round(s, 3), "GB_per_s": round(nbytes / s / 1e9, 4)}
+        tot_bytes += nbytes
+        tot_s += s
+
+    c3 = np.zeros(w3.num_blocks * w3.block_size * NV, np.uint8)
+    timed("nvfp4_ds_mla_write", n3 * (1152 + NV + 8),
+          lambda: oracle.write_nvfp4_ds_mla(w3.kv_c[:n3], w3.k_pe[:n3], c3, w3.slot_mapping[:n3],
+                                            w3.num_blocks, w3.block_size))
+    timed("nvfp4_ds_mla_gather", r3 * (NV + 1152),
+          lambda: oracle.gather_nvfp4_ds_mla(c3, r3, g3.block_table, g3.workspace_starts, g3.seq_starts,
+                                             g3.num_blocks, g3.block_size))
+    del c3
+    c4 = np.zeros(w4.num_blocks * w4.block_size * F8, np.uint8)
+    timed("fp8_ds_mla_write", n4 * (1152 + F8 + 8),
+          lambda: oracle.write_fp8_ds_mla(w4.kv_c[:n4], w4.k_pe[:n4], c4, w4.slot_mapping[:n4],
+                                          w4.num_blocks, w4.block_size))
+    timed("fp8_ds_mla_gather", r4 * (F8 + 1152),
+          lambda: oracle.gather_fp8_ds_mla(c4, r4, g4.block_table, g4.workspace_starts, g4.seq_starts,
+                                           g4.num_blocks, g4.block_size))
+    del c4
+    H, hs = w5.key.shape[1], w5.key.shape[2]
+    L = oracle.kv_layout_split(w5.block_size, H, hs)
+    c5 = np.zeros(w5.num_blocks * L.block_stride, np.uint8)
+    sl = w5.slot_mapping[:n5]
+    timed("nvfp4_kv_write", int((sl >= 0).sum()) * 5248 + n5 * 8,
+          lambda: oracle.reshape_and_cache_nvfp4(np.ascontiguousarray(w5.key[:n5]),
+                                                 np.ascontiguousarray(w5.value[:n5]), c5, sl, w5.num_blocks,
+                                                 w5.block_size, L, w5.k_scale, w5.v_scale))
+    r5 = min(n5, g5.total_tokens)
+    timed("nvfp4_kv_gather", r5 * 5248,
+          lambda: oracle.gather_upconvert_nvfp4_kv(c5, r5, g5.block_table, g5.workspace_starts, g5.seq_starts,
+                                                   H, hs, w5.num_blocks, w5.block_size, L, w5.k_scale,
+                                                   w5.v_scale))
+    return {"value": round(tot_bytes / tot_s / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {n3} / {n4} tokens of the nvfp4 / fp8 pre-fill writes, first {r3} / {r4} rows "
+                      f"of the nvfp4 / fp8 gathers, first {n5} tokens of the per-head write and {r5} rows "
+                      f"of its gather; single-threaded C oracle (-O2), {tot_s:.1f} s in total",
+            "per_op": res, "host_cpu": _cpu_name()}
+
+
+def _cpu_name():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+if __name__ == "__main__":
+    main()

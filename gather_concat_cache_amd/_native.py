@@ -1,0 +1,278 @@
+"""ctypes binding of libgcache.so (see include/gcache.h).
+
+Argument marshalling only: tensors are checked for dtype, device and layout,
+then their data pointers, strides and the current HIP stream are passed to the
+C entry point of the same name (without the ``gcache_`` prefix).  Every step
+of the computation runs in the HIP kernels; there is no CPU fallback, and
+importing this module fails when the library has not been built.
+"""
+import ctypes as C
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libgcache.so")
+
+STATUS = {0: "GCACHE_OK", -1: "GCACHE_ERR_NULL", -2: "GCACHE_ERR_SHAPE", -3: "GCACHE_ERR_ALIGN",
+          -4: "GCACHE_ERR_UNSUPPORTED", -5: "GCACHE_ERR_DEVICE", -6: "GCACHE_ERR_LAUNCH"}
+NVFP4_DS_MLA, FP8_DS_MLA = 0, 1
+
+
+class GcacheError(RuntimeError):
+    def __init__(self, status, fn):
+        lib = load()
+        msg = lib.gcache_status_string(status).decode()
+        super().__init__(f"{fn}: {STATUS.get(status, status)} ({msg})")
+        self.status = status
+
+
+class NvFp4KvLayout(C.Structure):
+    """gcache_nvfp4_kv_layout: byte offsets and strides of the per-head cache."""
+    _fields_ = [(n, C.c_int64) for n in (
+        "data_offset", "data_token_stride", "data_head_stride",
+        "scale_offset", "scale_token_stride", "scale_head_stride",
+        "side_stride", "block_stride")]
+
+
+_P, _I64, _I32 = C.c_void_p, C.c_int64, C.c_int32
+_SIGS = {
+    "gcache_entry_bytes": (_I64, [C.c_int]),
+    "gcache_nvfp4_full_dim": (_I32, [_I32]),
+    "gcache_status_string": (C.c_char_p, [C.c_int]),
+    "gcache_cache_write_nvfp4_ds_mla": (C.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _I64, _I32, _I64, _I64, _P]),
+    "gcache_cache_write_fp8_ds_mla": (C.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _I64, _I32, _I64, _I64, _P]),
+    "gcache_cache_gather_upconvert_nvfp4_ds_mla": (C.c_int, [_P, _P, _I64, _I64, _P, _I64, _P, _P, _I32, _I64,
+                                                            _I32, _I64, _I64, _P]),
+    "gcache_cache_gather_upconvert_fp8_ds_mla": (C.c_int, [_P, _P, _I64, _I64, _P, _I64, _P, _P, _I32, _I64,
+                                                          _I32, _I64, _I64, _P]),
+    "gcache_nvfp4_kv_split_layout": (C.c_int, [_I32, _I32, _I32, C.POINTER(NvFp4KvLayout)]),
+    "gcache_reshape_and_cache_nvfp4": (C.c_int, [_P, _P, _I64, _I64, _I64, _I64, _P, _P, _I64, _I32, _I32, _I64,
+                                                 _I32, C.POINTER(NvFp4KvLayout), _P, _P, _P]),
+    "gcache_gather_upconvert_nvfp4_kv": (C.c_int, [_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P, _I64, _P, _P,
+                                                   _I32, _I32, _I32, _I64, _I32, C.POINTER(NvFp4KvLayout), _P,
+                                                   _P, _P]),
+}
+
+_lib = None
+
+
+def load():
+    """Load libgcache.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m gather_concat_cache_amd.build` (hipcc, gfx950)")
+        lib = C.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(lib, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = lib
+    return _lib
+
+
+def _check(status, fn):
+    if status != 0:
+        raise GcacheError(status, fn)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _dev_tensor(t, dtype, name, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    return t
+
+
+def _stream(device, stream):
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return s.cuda_stream
+
+
+def entry_bytes(fmt):
+    """Bytes per token: 352 for NVFP4_DS_MLA, 656 for FP8_DS_MLA."""
+    return load().gcache_entry_bytes(fmt)
+
+
+def nvfp4_full_dim(head_size):
+    return load().gcache_nvfp4_full_dim(head_size)
+
+
+def nvfp4_kv_split_layout(block_size, num_heads, head_size):
+    L = NvFp4KvLayout()
+    _check(load().gcache_nvfp4_kv_split_layout(block_size, num_heads, head_size, C.byref(L)),
+           "nvfp4_kv_split_layout")
+    return L
+
+
+# ---------------------------------------------------------------------------
+def _ds_cache_geometry(kv_cache, name):
+    """kv_cache: uint8 [num_blocks, block_size, entry_stride-or-more] with unit
+    last stride -> (num_blocks, block_size, block_stride, entry_stride)."""
+    if kv_cache.dim() != 3 or kv_cache.stride(2) != 1:
+        raise ValueError(f"{name}: expected uint8 [num_blocks, block_size, entry] with unit last stride")
+    return kv_cache.shape[0], kv_cache.shape[1], kv_cache.stride(0), kv_cache.stride(1)
+
+
+def _ds_write(fn_name, kv_c, k_pe, kv_cache, slot_mapping, stream):
+    dev = _dev_tensor(kv_cache, torch.uint8, "kv_cache").device
+    _dev_tensor(kv_c, torch.bfloat16, "kv_c", dev)
+    _dev_tensor(k_pe, torch.bfloat16, "k_pe", dev)
+    _dev_tensor(slot_mapping, torch.int64, "slot_mapping", dev)
+    T = slot_mapping.numel()
+    if T == 0:
+        return                                   # no tokens: nothing to do
+    if kv_c.dim() != 2 or k_pe.dim() != 2 or kv_c.stride(1) != 1 or k_pe.stride(1) != 1:
+        raise ValueError("kv_c and k_pe must be 2-D with unit last stride")
+    if kv_c.shape[0] < T or k_pe.shape[0] < T or kv_c.shape[1] < 512 or k_pe.shape[1] < 64:
+        raise ValueError("kv_c must be [T, >=512] and k_pe [T, >=64]")
+    if not slot_mapping.is_contiguous():
+        raise ValueError("slot_mapping must be contiguous")
+    nb, bs, bstr, estr = _ds_cache_geometry(kv_cache, "kv_cache")
+    with torch.cuda.device(dev):
+        st = getattr(load(), fn_name)(_ptr(kv_c), _ptr(k_pe), _ptr(kv_cache), _ptr(slot_mapping), T,
+                                      kv_c.stride(0), k_pe.stride(0), nb, bs, bstr, estr,
+                                      _stream(dev, stream))
+    _check(st, fn_name)
+
+
+def cache_write_nvfp4_ds_mla(kv_c, k_pe, kv_cache, slot_mapping, stream=None):
+    """Quantize kv_c bf16 [T,512] and k_pe bf16 [T,64] into the nvfp4_ds_mla
+    cache uint8 [num_blocks, block_size, >=352] at slot_mapping (int64 [T],
+    < 0 skipped).  Enqueued on the current stream (or `stream`)."""
+    _ds_write("gcache_cache_write_nvfp4_ds_mla", kv_c, k_pe, kv_cache, slot_mapping, stream)
+
+
+def cache_write_fp8_ds_mla(kv_c, k_pe, kv_cache, slot_mapping, stream=None):
+    """fp8_ds_mla write into uint8 [num_blocks, block_size, >=656]."""
+    _ds_write("gcache_cache_write_fp8_ds_mla", kv_c, k_pe, kv_cache, slot_mapping, stream)
+
+
+def _ds_gather(fn_name, src_cache, dst, block_table, workspace_starts, seq_starts, batch_size, stream):
+    dev = _dev_tensor(src_cache, torch.uint8, "src_cache").device
+    _dev_tensor(dst, torch.bfloat16, "dst", dev)
+    _dev_tensor(block_table, torch.int32, "block_table", dev)
+    _dev_tensor(workspace_starts, torch.int32, "workspace_starts", dev)
+    if seq_starts is not None:
+        _dev_tensor(seq_starts, torch.int32, "seq_starts", dev)
+    if dst.dim() == 2 and dst.shape[0] == 0:
+        return                                   # no rows: nothing to do
+    if dst.dim() != 2 or dst.stride(1) != 1 or dst.shape[1] < 576:
+        raise ValueError("dst must be bf16 [total_tokens, >=576] with unit last stride")
+    if block_table.dim() != 2 or block_table.stride(1) != 1:
+        raise ValueError("block_table must be int32 [batch, max_blocks] with unit last stride")
+    B = workspace_starts.numel() if batch_size is None else int(batch_size)
+    if B > workspace_starts.numel() or (seq_starts is not None and B > seq_starts.numel()) \
+            or B > block_table.shape[0]:
+        raise ValueError("batch_size exceeds workspace_starts / seq_starts / block_table")
+    nb, bs, bstr, estr = _ds_cache_geometry(src_cache, "src_cache")
+    with torch.cuda.device(dev):
+        st = getattr(load(), fn_name)(_ptr(src_cache), _ptr(dst), dst.shape[0], dst.stride(0),
+                                      _ptr(block_table), block_table.stride(0), _ptr(workspace_starts),
+                                      _ptr(seq_starts), B, nb, bs, bstr, estr, _stream(dev, stream))
+    _check(st, fn_name)
+
+
+def cache_gather_upconvert_nvfp4_ds_mla(src_cache, dst, block_table, workspace_starts,
+                                        seq_starts=None, batch_size=None, stream=None):
+    """Gather-upconvert nvfp4_ds_mla entries into dst bf16 [total_tokens, 576]:
+    row r of request b (ws[b] <= r < ws[b+1]) reads position
+    seq_starts[b] + r - ws[b] through block_table[b]."""
+    _ds_gather("gcache_cache_gather_upconvert_nvfp4_ds_mla", src_cache, dst, block_table,
+               workspace_starts, seq_starts, batch_size, stream)
+
+
+def cache_gather_upconvert_fp8_ds_mla(src_cache, dst, block_table, workspace_starts,
+                                      seq_starts=None, batch_size=None, stream=None):
+    """fp8_ds_mla gather-upconvert into dst bf16 [total_tokens, 576]."""
+    _ds_gather("gcache_cache_gather_upconvert_fp8_ds_mla", src_cache, dst, block_table,
+               workspace_starts, seq_starts, batch_size, stream)
+
+
+# ---------------------------------------------------------------------------
+def _kv_geometry(kv_cache, num_heads, head_size, layout):
+    """kv_cache uint8 [num_blocks, 2, block_size, H, full_dim] -> (nb, bs, layout)."""
+    if kv_cache.dim() != 5 or kv_cache.shape[1] != 2:
+        raise ValueError("kv_cache must be uint8 [num_blocks, 2, block_size, num_heads, full_dim]")
+    nb, bs = kv_cache.shape[0], kv_cache.shape[2]
+    if layout is None:
+        if not kv_cache.is_contiguous():
+            raise ValueError("the default split layout needs a contiguous kv_cache")
+        layout = nvfp4_kv_split_layout(bs, num_heads, head_size)
+    return nb, bs, layout
+
+
+def _scale(t, name, dev):
+    _dev_tensor(t, torch.float32, name, dev)
+    if t.numel() != 1:
+        raise ValueError(f"{name} must hold one fp32 value")
+    return t
+
+
+def reshape_and_cache_nvfp4(key, value, kv_cache, slot_mapping, k_scale, v_scale, layout=None,
+                            stream=None):
+    """Per-head NVFP4 write of key / value bf16 [T, H, hs] into kv_cache uint8
+    [num_blocks, 2, block_size, H, hs/2 + hs/16] (split layout unless a
+    NvFp4KvLayout is given); k_scale / v_scale: fp32 device scalars."""
+    dev = _dev_tensor(kv_cache, torch.uint8, "kv_cache").device
+    _dev_tensor(key, torch.bfloat16, "key", dev)
+    _dev_tensor(value, torch.bfloat16, "value", dev)
+    _dev_tensor(slot_mapping, torch.int64, "slot_mapping", dev)
+    _scale(k_scale, "k_scale", dev)
+    _scale(v_scale, "v_scale", dev)
+    if key.dim() != 3 or value.shape != key.shape or key.stride(2) != 1 or value.stride(2) != 1:
+        raise ValueError("key / value must be bf16 [T, H, hs] with unit last stride")
+    T, H, hs = key.shape
+    if slot_mapping.numel() == 0:
+        return
+    if slot_mapping.numel() > T or not slot_mapping.is_contiguous():
+        raise ValueError("slot_mapping must be contiguous with at most T entries")
+    nb, bs, layout = _kv_geometry(kv_cache, H, hs, layout)
+    with torch.cuda.device(dev):
+        st = load().gcache_reshape_and_cache_nvfp4(
+            _ptr(key), _ptr(value), key.stride(0), key.stride(1), value.stride(0), value.stride(1),
+            _ptr(kv_cache), _ptr(slot_mapping), slot_mapping.numel(), H, hs, nb, bs, C.byref(layout),
+            _ptr(k_scale), _ptr(v_scale), _stream(dev, stream))
+    _check(st, "reshape_and_cache_nvfp4")
+
+
+def gather_upconvert_nvfp4_kv(kv_cache, key_out, value_out, block_table, workspace_starts,
+                              k_scale, v_scale, seq_starts=None, batch_size=None, layout=None,
+                              stream=None):
+    """Per-head NVFP4 gather-upconvert into key_out / value_out bf16
+    [total_tokens, H, hs] through the DS-MLA gather walk."""
+    dev = _dev_tensor(kv_cache, torch.uint8, "kv_cache").device
+    _dev_tensor(key_out, torch.bfloat16, "key_out", dev)
+    _dev_tensor(value_out, torch.bfloat16, "value_out", dev)
+    _dev_tensor(block_table, torch.int32, "block_table", dev)
+    _dev_tensor(workspace_starts, torch.int32, "workspace_starts", dev)
+    if seq_starts is not None:
+        _dev_tensor(seq_starts, torch.int32, "seq_starts", dev)
+    _scale(k_scale, "k_scale", dev)
+    _scale(v_scale, "v_scale", dev)
+    if key_out.dim() != 3 or value_out.shape != key_out.shape or key_out.stride(2) != 1 \
+            or value_out.stride(2) != 1:
+        raise ValueError("key_out / value_out must be bf16 [total, H, hs] with unit last stride")
+    if block_table.dim() != 2 or block_table.stride(1) != 1:
+        raise ValueError("block_table must be int32 [batch, max_blocks] with unit last stride")
+    total, H, hs = key_out.shape
+    if total == 0:
+        return
+    B = workspace_starts.numel() if batch_size is None else int(batch_size)
+    nb, bs, layout = _kv_geometry(kv_cache, H, hs, layout)
+    with torch.cuda.device(dev):
+        st = load().gcache_gather_upconvert_nvfp4_kv(
+            _ptr(kv_cache), _ptr(key_out), _ptr(value_out), total, key_out.stride(0), key_out.stride(1),
+            value_out.stride(0), value_out.stride(1), _ptr(block_table), block_table.stride(0),
+            _ptr(workspace_starts), _ptr(seq_starts), B, H, hs, nb, bs, C.byref(layout),
+            _ptr(k_scale), _ptr(v_scale), _stream(dev, stream))
+    _check(st, "gather_upconvert_nvfp4_kv")

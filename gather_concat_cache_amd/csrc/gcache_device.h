@@ -1,0 +1,118 @@
+// gcache_device.h -- device helpers shared by the gfx950 kernels.
+//
+// Conversions use the gfx950 hardware converters.  Each one was checked
+// exhaustively against round-to-nearest-even over every non-NaN binary32
+// input (scale operand 1.0; see the design notes for the sweep):
+//   v_cvt_scalef32_pk_fp4_f32  e2m1, RN-even, saturating at +-6, sign kept
+//                              (-0 and tiny negatives give 0x8); the first
+//                              operand lands in the low nibble.
+//   v_cvt_pk_fp8_f32           OCP e4m3, RN-even, sign kept; it does NOT
+//                              saturate (NaN above 464), so inputs are
+//                              clamped to +-448 with v_med3_f32 first, which
+//                              keeps -0 and denormals.
+//   v_cvt_pk_bf16_f32          RN-even (used for the rounding f32 -> bf16).
+//   v_cvt_scalef32_pk_f32_fp4, v_cvt_pk_f32_fp8: exact decoders.
+// The scale operand of the scalef32 forms only carries a power of two (its
+// exponent field), so it is always 1.0 here and block scales are applied
+// with ordinary binary32 multiplies.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gcache {
+
+constexpr int kWave = 64;
+constexpr int kBlockThreads = 256;                 // 4 waves per workgroup
+constexpr int kWavesPerBlock = kBlockThreads / kWave;
+
+// DS-MLA geometry: [vLLM PR #51724 digest, "Implementation breakdown" 2-3].
+constexpr int kNope = 512;
+constexpr int kRope = 64;
+constexpr int kRow = kNope + kRope;                // gathered workspace row
+constexpr int kNvEntry = 352;
+constexpr int kNvRopeOff = 256;
+constexpr int kNvScaleOff = 320;
+constexpr int kF8Entry = 656;
+constexpr int kF8ScaleOff = 512;
+constexpr int kF8RopeOff = 528;
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ int lane_id() {
+    return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+}
+// Wave index inside the workgroup, as a wave-uniform (scalar) value.
+__device__ __forceinline__ int wave_id() {
+    return __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+}
+
+// bf16 pair in one dword -> binary32 (exact).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Two values -> e2m1 codes packed into byte SEL of `old` (lo -> low nibble).
+template <int SEL>
+__device__ __forceinline__ uint32_t put_e2m1x2(uint32_t old, float lo, float hi) {
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, lo, hi, 1.0f, SEL);
+}
+
+__device__ __forceinline__ float clamp_e4m3(float v) {
+    return __builtin_amdgcn_fmed3f(v, 448.0f, -448.0f);
+}
+// Two values -> e4m3 codes in 16-bit word HI of `old` (lo -> lower byte).
+template <bool HI>
+__device__ __forceinline__ uint32_t put_e4m3x2(uint32_t old, float lo, float hi) {
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(clamp_e4m3(lo), clamp_e4m3(hi), (int)old, HI);
+}
+
+// Byte SEL of `packed` (two e2m1 codes) -> two binary32 (exact).
+template <int SEL>
+__device__ __forceinline__ f32x2 e2m1x2_f32(uint32_t packed) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(packed, 1.0f, SEL);
+}
+// Word HI of `packed` (two e4m3 codes) -> two binary32 (exact).
+template <bool HI>
+__device__ __forceinline__ f32x2 e4m3x2_f32(uint32_t packed) {
+    return __builtin_amdgcn_cvt_pk_f32_fp8((int)packed, HI);
+}
+// Low byte of `b` (one e4m3 code) -> binary32 (exact).
+__device__ __forceinline__ float e4m3_f32(uint32_t b) { return e4m3x2_f32<false>(b).x; }
+
+// Two binary32 -> bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    bf16x2 v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// Split a slot (or logical position) into (block, offset).  `shift` >= 0
+// when block_size is a power of two.
+struct BlockDiv {
+    int64_t size;
+    int shift;
+};
+__device__ __forceinline__ void split_block(int64_t pos, const BlockDiv& d, int64_t& blk,
+                                            int64_t& off) {
+    if (d.shift >= 0) {
+        blk = pos >> d.shift;
+        off = pos & (d.size - 1);
+    } else {
+        blk = pos / d.size;
+        off = pos - blk * d.size;
+    }
+}
+
+// Gather walk: request of workspace row r = the largest b < batch with
+// ws[b] <= r (binary search; ws non-decreasing, ws[0] == 0).
+__device__ __forceinline__ int find_request(const int32_t* __restrict__ ws, int batch, int64_t r) {
+    int lo = 0, hi = batch;                        // ws[lo] <= r, answer in [lo, hi)
+    while (hi - lo > 1) {
+        int mid = (lo + hi) >> 1;
+        if ((int64_t)ws[mid] <= r) lo = mid; else hi = mid;
+    }
+    return lo;
+}
+
+}  // namespace gcache

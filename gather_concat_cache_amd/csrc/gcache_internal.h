@@ -1,0 +1,96 @@
+// gcache_internal.h -- kernel parameter blocks and launchers (host side).
+// The extern "C" entry points in gcache_abi.hip validate arguments, then
+// fill one of these structs and call the matching launcher.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gcache_device.h"
+
+namespace gcache {
+
+struct DsMlaWriteParams {
+    const uint16_t* kv_c;        // bf16 [T, >=512]
+    const uint16_t* k_pe;        // bf16 [T, >=64]
+    uint8_t* cache;
+    const int64_t* slots;        // [T], < 0 = padding
+    int64_t num_tokens;
+    int64_t kv_c_stride, k_pe_stride;   // elements
+    int64_t block_stride, entry_stride; // bytes
+    BlockDiv div;                // block_size
+};
+
+struct DsMlaGatherParams {
+    const uint8_t* cache;
+    uint16_t* dst;               // bf16 [total, >=576]
+    int64_t total, dst_stride;
+    const int32_t* block_table;
+    int64_t bt_stride;
+    const int32_t* ws;           // workspace_starts [batch]
+    const int32_t* seq_starts;   // [batch] or nullptr
+    int32_t batch;
+    int64_t block_stride, entry_stride;
+    BlockDiv div;
+};
+
+struct KvLayout {                // mirrors gcache_nvfp4_kv_layout (bytes)
+    int64_t data_offset, data_token_stride, data_head_stride;
+    int64_t scale_offset, scale_token_stride, scale_head_stride;
+    int64_t side_stride, block_stride;
+};
+
+struct KvWriteParams {
+    const uint16_t* src[2];      // key, value: bf16 [T, H, hs]
+    int64_t token_stride[2], head_stride[2];  // elements
+    uint8_t* cache;
+    const int64_t* slots;
+    int64_t num_tokens;
+    int32_t num_heads, head_size;
+    int32_t bph_shift;           // log2(head_size / 16), or -1
+    BlockDiv div;
+    KvLayout L;
+    const float* gscale[2];      // k_scale, v_scale (device scalars)
+};
+
+struct KvGatherParams {
+    const uint8_t* cache;
+    uint16_t* out[2];            // key_out, value_out: bf16 [total, H, hs]
+    int64_t token_stride[2], head_stride[2];
+    int64_t total;
+    const int32_t* block_table;
+    int64_t bt_stride;
+    const int32_t* ws;
+    const int32_t* seq_starts;
+    int32_t batch;
+    int32_t num_heads, head_size;
+    int32_t cph_shift;           // log2(head_size / 8), or -1
+    BlockDiv div;
+    KvLayout L;
+    const float* gscale[2];
+};
+
+hipError_t launch_write_nvfp4_ds_mla(const DsMlaWriteParams& p, hipStream_t s);
+hipError_t launch_write_fp8_ds_mla(const DsMlaWriteParams& p, hipStream_t s);
+hipError_t launch_gather_nvfp4_ds_mla(const DsMlaGatherParams& p, hipStream_t s);
+hipError_t launch_gather_fp8_ds_mla(const DsMlaGatherParams& p, hipStream_t s);
+hipError_t launch_reshape_and_cache_nvfp4(const KvWriteParams& p, hipStream_t s);
+hipError_t launch_gather_nvfp4_kv(const KvGatherParams& p, hipStream_t s);
+
+// Workgroups for `waves` independent wave-sized work items (grid-stride
+// loops cover anything beyond the cap).
+inline unsigned grid_for_waves(int64_t waves) {
+    int64_t blocks = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
+    const int64_t cap = int64_t(1) << 22;
+    if (blocks < 1) blocks = 1;
+    return (unsigned)(blocks < cap ? blocks : cap);
+}
+
+template <typename P>
+inline hipError_t launch1(void (*kernel)(P), unsigned blocks, hipStream_t s, const P& p) {
+    void* args[] = {const_cast<P*>(&p)};
+    return hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3(blocks), dim3(kBlockThreads),
+                           args, 0, s);
+}
+
+}  // namespace gcache

@@ -149,17 +149,25 @@ def nvfp4_full_dim(head_size):
 
 
 # ---- DS-MLA write / gather -----------------------------------------------
+def _rows(a, dtype, name):
+    """2-D array whose rows may be strided (a slice of a wider buffer):
+    returns the row stride in elements."""
+    if a.dtype != dtype or a.ndim != 2 or a.strides[1] != a.itemsize or a.strides[0] % a.itemsize:
+        raise ValueError(f"{name}: expected a 2-D {np.dtype(dtype)} array with unit inner stride")
+    return a.strides[0] // a.itemsize
+
+
 def _write(fn, what, kv_c, k_pe, cache, slot_mapping, num_blocks, block_size,
            block_stride, entry_stride):
-    kv_c = _need(kv_c, np.uint16, "kv_c")
-    k_pe = _need(k_pe, np.uint16, "k_pe")
+    kv_stride = _rows(kv_c, np.uint16, "kv_c")
+    pe_stride = _rows(k_pe, np.uint16, "k_pe")
     cache = _need(cache, np.uint8, "cache")
     slot_mapping = _need(slot_mapping, np.int64, "slot_mapping")
     T = slot_mapping.shape[0]
-    if kv_c.shape[0] < T or k_pe.shape[0] < T:
-        raise ValueError("kv_c/k_pe have fewer rows than slot_mapping")
+    if kv_c.shape[0] < T or k_pe.shape[0] < T or kv_c.shape[1] < NOPE_DIM or k_pe.shape[1] < ROPE_DIM:
+        raise ValueError("kv_c must be [T, >=512] and k_pe [T, >=64]")
     _check(fn(_ptr(kv_c), _ptr(k_pe), _ptr(cache), cache.size, _ptr(slot_mapping), T,
-              kv_c.shape[1], k_pe.shape[1], num_blocks, block_size, block_stride, entry_stride),
+              kv_stride, pe_stride, num_blocks, block_size, block_stride, entry_stride),
            what)
 
 

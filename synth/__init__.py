@@ -37,6 +37,32 @@ def _normal_bf16(rng, shape):
     return bf16_bits(rng.standard_normal(shape, dtype=np.float32))
 
 
+CHUNK_ROWS = 8192
+
+
+def normal_bf16_rows(seed, stream, rows, cols):
+    """N(0,1) bf16 bits [rows, cols], drawn in chunks of CHUNK_ROWS rows;
+    chunk c uses its own generator default_rng([seed, stream, c]), so the
+    result does not depend on how many threads fill it."""
+    import concurrent.futures as cf
+    import os
+    out = np.empty((rows, cols), np.uint16)
+    nchunks = (rows + CHUNK_ROWS - 1) // CHUNK_ROWS
+
+    def fill(c):
+        lo, hi = c * CHUNK_ROWS, min(rows, (c + 1) * CHUNK_ROWS)
+        x = np.random.default_rng([seed, stream, c]).standard_normal((hi - lo, cols), dtype=np.float32)
+        u = x.view(np.uint32)
+        lsb = (u >> np.uint32(16)) & np.uint32(1)
+        u += np.uint32(0x7FFF)
+        u += lsb
+        np.right_shift(u, np.uint32(16), out=u)
+        out[lo:hi] = u
+    with cf.ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 4)) as ex:
+        list(ex.map(fill, range(nchunks)))
+    return out
+
+
 def padded_slots(rng, num_slots, num_tokens, pad_count, sequential=False):
     """Distinct slots (random draw without replacement, or 0..T-1), with
     exactly ``pad_count`` tokens (chosen without replacement) set to -1."""
@@ -125,8 +151,9 @@ def per_token_gather(name, slot_mapping, num_blocks, block_size):
 
 
 # ---------------------------------------------------------------------------
-# The named workloads.  Seed of workload k is 1000 + k; a pre-fill write and
-# the gather over it use streams 0 and 1 of that seed.
+# The named workloads.  Seed of workload k is 1000 + k; a pre-fill write
+# draws NoPE from stream 0 and RoPE from stream 2 of that seed (row-chunked,
+# see normal_bf16_rows), the gather over it uses stream 1.
 # ---------------------------------------------------------------------------
 def config1():
     """Tiny round trip: 64 N(0,1) tokens, cache 8 x 64 x 352, 10% padding (6
@@ -161,10 +188,9 @@ def config2():
 def config3_prefill():
     """Pre-fill of the prefill-gather cache: 524288 N(0,1) tokens into every
     slot of 8192 blocks x 64 (slot_mapping = arange, no padding)."""
-    rng = _rng(1003, 0)
     T = 8192 * 64
-    return WriteCase("c3w-prefill-write", _normal_bf16(rng, (T, NOPE)),
-                     _normal_bf16(rng, (T, ROPE)), np.arange(T, dtype=np.int64), 8192, 64)
+    return WriteCase("c3w-prefill-write", normal_bf16_rows(1003, 0, T, NOPE),
+                     normal_bf16_rows(1003, 2, T, ROPE), np.arange(T, dtype=np.int64), 8192, 64)
 
 
 def config3_gather():
@@ -175,10 +201,9 @@ def config3_gather():
 
 def config4_prefill():
     """fp8_ds_mla pre-fill: 1048576 N(0,1) tokens into every slot of 16384 x 64."""
-    rng = _rng(1004, 0)
     T = 16384 * 64
-    return WriteCase("c4w-fp8-prefill-write", _normal_bf16(rng, (T, NOPE)),
-                     _normal_bf16(rng, (T, ROPE)), np.arange(T, dtype=np.int64), 16384, 64)
+    return WriteCase("c4w-fp8-prefill-write", normal_bf16_rows(1004, 0, T, NOPE),
+                     normal_bf16_rows(1004, 2, T, ROPE), np.arange(T, dtype=np.int64), 16384, 64)
 
 
 def config4_gather():

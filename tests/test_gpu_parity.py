@@ -1,0 +1,257 @@
+"""GPU parity: every HIP entry point, called through the C ABI (Python
+binding), against the CPU oracle on the same seeded inputs -- bit-exact on
+every cache byte (sentinel-filled, so untouched bytes are checked too) and
+every bf16 output bit.  Sizes span several workgroups and ragged tails; the
+full-size workloads run in the launch configuration the benchmark times.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from gpu_util import assert_same, dev, filled_cache, host
+
+pytestmark = pytest.mark.gpu
+
+NV, F8 = 352, 656
+
+
+@pytest.fixture(scope="module")
+def g():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gather_concat_cache_amd as gc
+    return gc
+
+
+def _ds_pair(fmt):
+    import gather_concat_cache_amd as gc
+    if fmt == "nvfp4":
+        return NV, gc.cache_write_nvfp4_ds_mla, gc.cache_gather_upconvert_nvfp4_ds_mla
+    return F8, gc.cache_write_fp8_ds_mla, gc.cache_gather_upconvert_fp8_ds_mla
+
+
+def _orc_ds(orc, fmt):
+    if fmt == "nvfp4":
+        return orc.write_nvfp4_ds_mla, orc.gather_nvfp4_ds_mla
+    return orc.write_fp8_ds_mla, orc.gather_fp8_ds_mla
+
+
+def _cache_view(flat, nb, bs, bstr, estr):
+    return torch.as_strided(flat, (nb, bs, estr), (bstr, estr, 1))
+
+
+def run_ds_write(orc, fmt, kv_c, k_pe, slots, nb, bs, bstr=None, estr=None, fill=0xA5,
+                 kv_dev=None, pe_dev=None):
+    """GPU write vs oracle write into identically pre-filled flat caches.
+    Returns the oracle's cache (the expected bytes)."""
+    eb, gwrite, _ = _ds_pair(fmt)
+    owrite, _ = _orc_ds(orc, fmt)
+    estr = estr or eb
+    bstr = bstr or bs * estr
+    want = np.full(nb * bstr, fill, np.uint8)
+    owrite(kv_c, k_pe, want, slots, nb, bs, bstr, estr)
+    flat = filled_cache((nb * bstr,), fill)
+    gwrite(kv_dev if kv_dev is not None else dev(kv_c), pe_dev if pe_dev is not None else dev(k_pe),
+           _cache_view(flat, nb, bs, bstr, estr), dev(slots))
+    torch.cuda.synchronize()
+    assert_same(host(flat), want, f"{fmt} write cache bytes")
+    return want, flat
+
+
+def run_ds_gather(orc, fmt, cache_np, cache_dev, gcase, nb, bs, bstr=None, estr=None, dst_stride=576,
+                  seq_starts=True):
+    eb, _, ggather = _ds_pair(fmt)
+    _, ogather = _orc_ds(orc, fmt)
+    estr = estr or eb
+    bstr = bstr or bs * estr
+    ss = gcase.seq_starts if seq_starts else None
+    want = np.full((gcase.total_tokens, dst_stride), 0x7FC1, np.uint16)
+    ogather(cache_np, gcase.total_tokens, gcase.block_table, gcase.workspace_starts, ss, nb, bs, bstr,
+            estr, dst=want)
+    dst = dev(np.full((gcase.total_tokens, dst_stride), 0x7FC1, np.uint16))
+    ggather(_cache_view(cache_dev, nb, bs, bstr, estr), dst, dev(gcase.block_table),
+            dev(gcase.workspace_starts), None if ss is None else dev(ss))
+    torch.cuda.synchronize()
+    assert_same(host(dst), want, f"{fmt} gather ({gcase.name})")
+
+
+# ---------------------------------------------------------------------------
+# nvfp4_ds_mla and fp8_ds_mla
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("fmt", ["nvfp4", "fp8"])
+def test_config1_round_trip(g, orc, fmt):
+    w, g_tok, g_all = synth.config1()
+    want, flat = run_ds_write(orc, fmt, w.kv_c, w.k_pe, w.slot_mapping, 8, 64)
+    for gc_ in (g_tok, g_all):
+        run_ds_gather(orc, fmt, want, flat, gc_, 8, 64)
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "fp8"])
+def test_config2_decode_write(g, orc, fmt):
+    w = synth.config2()
+    run_ds_write(orc, fmt, w.kv_c, w.k_pe, w.slot_mapping, w.num_blocks, w.block_size)
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "fp8"])
+def test_ragged_strided_non_pow2_block(g, orc, fmt):
+    """Odd token count, kv_c / k_pe as slices of one [T, 584] buffer, block
+    size 48 (the generic division path), padded entries (entry_stride >
+    entry) and gaps between blocks; gathers with empty requests, a wider dst
+    row stride, with and without seq_starts."""
+    rng = np.random.default_rng(77)
+    eb = NV if fmt == "nvfp4" else F8
+    T, nb, bs = 1001, 30, 48
+    estr = eb + 32
+    bstr = bs * estr + 256
+    buf = synth.bf16_bits(rng.standard_normal((T, 584), dtype=np.float32)
+                          * np.exp(rng.standard_normal((T, 1), dtype=np.float32)))
+    kv_c, k_pe = buf[:, :512], buf[:, 520:584]
+    slots = synth.padded_slots(rng, nb * bs, T, 37)
+    bdev = dev(buf)
+    want, flat = run_ds_write(orc, fmt, kv_c, k_pe, slots, nb, bs, bstr, estr,
+                              kv_dev=bdev[:, :512], pe_dev=bdev[:, 520:584])
+    # requests: lengths with empty requests in between, arbitrary seq_starts
+    L = np.array([100, 0, 333, 1, 0, 200, 47, 480, 0], np.int64)
+    s = np.array([5, 0, 100, 0, 0, 199, 0, 3, 0], np.int64)
+    rows = np.where(L > 0, L - s, 0)
+    perm = rng.permutation(nb).astype(np.int32)
+    bt = np.full((9, 12), -1, np.int32)
+    pos = 0
+    for b in range(9):
+        n = -(-int(L[b]) // bs)
+        bt[b, :n] = perm[pos:pos + n]
+        pos += n
+    assert pos <= nb
+    ws = np.concatenate([[0], np.cumsum(rows)[:-1]]).astype(np.int32)
+    gcase = synth.GatherCase("ragged", bt, ws, s.astype(np.int32), int(rows.sum()), nb, bs, L)
+    assert gcase.total_tokens % 16 != 0
+    run_ds_gather(orc, fmt, want, flat, gcase, nb, bs, bstr, estr, dst_stride=600)
+    g0 = synth.GatherCase("ragged-no-starts", bt, ws, np.zeros(9, np.int32), int(rows.sum()), nb, bs, L)
+    run_ds_gather(orc, fmt, want, flat, g0, nb, bs, bstr, estr, seq_starts=False)
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "fp8"])
+def test_edge_cases(g, orc, fmt):
+    eb, gwrite, ggather = _ds_pair(fmt)
+    rng = np.random.default_rng(3)
+    kv_c = synth.bf16_bits(rng.standard_normal((5, 512), dtype=np.float32))
+    k_pe = synth.bf16_bits(rng.standard_normal((5, 64), dtype=np.float32))
+    # all padding: nothing is written
+    run_ds_write(orc, fmt, kv_c, k_pe, np.full(5, -1, np.int64), 2, 16)
+    # one token, into the very last slot
+    run_ds_write(orc, fmt, kv_c[:1], k_pe[:1], np.array([31], np.int64), 2, 16)
+    # zero tokens / zero rows: no-ops that touch nothing
+    flat = filled_cache((2 * 16 * eb,), 0x33)
+    gwrite(dev(kv_c[:0]), dev(k_pe[:0]), _cache_view(flat, 2, 16, 16 * eb, eb), dev(np.zeros(0, np.int64)))
+    ggather(_cache_view(flat, 2, 16, 16 * eb, eb), dev(np.zeros((0, 576), np.uint16)),
+            dev(np.zeros((1, 2), np.int32)), dev(np.zeros(1, np.int32)))
+    torch.cuda.synchronize()
+    assert np.all(host(flat) == 0x33)
+    # zero and negative-zero blocks, saturating magnitudes, subnormal scales
+    x = np.zeros((4, 512), np.float32)
+    x[1, :16] = -0.0
+    x[2] = rng.standard_normal(512).astype(np.float32) * np.float32(3e4)
+    x[3] = rng.standard_normal(512).astype(np.float32) * np.float32(1e-4)
+    run_ds_write(orc, fmt, synth.bf16_bits(x), k_pe[:4], np.arange(4, dtype=np.int64), 1, 4)
+    with pytest.raises(g.GcacheError):                       # misaligned row stride
+        gwrite(dev(np.zeros((2, 516), np.uint16))[:, :512], dev(k_pe[:2]),
+               _cache_view(flat, 2, 16, 16 * eb, eb), dev(np.zeros(2, np.int64)))
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "fp8"])
+def test_full_size_prefill_write_and_gather(g, orc, fmt):
+    """The benchmark's workloads: the 524288-token (nvfp4) / 1048576-token
+    (fp8) pre-fill writes and the 16- / 32-request prefill gathers, whole
+    cache and whole workspace compared."""
+    w = synth.config3_prefill() if fmt == "nvfp4" else synth.config4_prefill()
+    gcase = synth.config3_gather() if fmt == "nvfp4" else synth.config4_gather()
+    want, flat = run_ds_write(orc, fmt, w.kv_c, w.k_pe, w.slot_mapping, w.num_blocks, w.block_size)
+    del w
+    run_ds_gather(orc, fmt, want, flat, gcase, gcase.num_blocks, gcase.block_size)
+
+
+# ---------------------------------------------------------------------------
+# per-head NVFP4 K/V
+# ---------------------------------------------------------------------------
+def _kv_case(rng, T, H, hs, nb, bs, pad):
+    mag_k = rng.uniform(0.1, 10, (1, H, 1)).astype(np.float32)
+    key = synth.bf16_bits(rng.standard_normal((T, H, hs), dtype=np.float32) * mag_k)
+    value = synth.bf16_bits(rng.standard_normal((T, H, hs), dtype=np.float32) * np.float32(0.05))
+    slots = synth.padded_slots(rng, nb * bs, T, pad)
+    return key, value, slots
+
+
+def run_kv(orc, g, key, value, slots, nb, bs, L_orc, L_gpu, ks, vs, key_dev=None, value_dev=None,
+           out_hnd=False):
+    T, H, hs = key.shape
+    side = max(L_orc.side_stride, 1)
+    size = nb * L_orc.block_stride
+    want = np.full(size, 0xA5, np.uint8)
+    orc.reshape_and_cache_nvfp4(key, value, want, slots, nb, bs, L_orc, ks, vs)
+    flat = filled_cache((size,), 0xA5)
+    fd = hs // 2 + hs // 16
+    cache5 = torch.as_strided(flat, (nb, 2, bs, H, fd), (L_orc.block_stride, side, H * fd, fd, 1))
+    ks_d = torch.tensor([ks], dtype=torch.float32, device="cuda")
+    vs_d = torch.tensor([vs], dtype=torch.float32, device="cuda")
+    g.reshape_and_cache_nvfp4(key_dev if key_dev is not None else dev(key),
+                              value_dev if value_dev is not None else dev(value),
+                              cache5, dev(slots), ks_d, vs_d, layout=L_gpu)
+    torch.cuda.synchronize()
+    assert_same(host(flat), want, "per-head write cache bytes")
+    gcase = synth.per_token_gather("kv", slots, nb, bs)
+    ok, ov = orc.gather_upconvert_nvfp4_kv(want, gcase.total_tokens, gcase.block_table,
+                                           gcase.workspace_starts, gcase.seq_starts, H, hs, nb, bs,
+                                           L_orc, ks, vs)
+    n = gcase.total_tokens
+    if out_hnd:   # outputs as [H, n, hs] memory viewed as [n, H, hs]
+        kb = torch.zeros((H, n, hs), dtype=torch.bfloat16, device="cuda")
+        vb = torch.zeros((H, n, hs), dtype=torch.bfloat16, device="cuda")
+        ko, vo = kb.permute(1, 0, 2), vb.permute(1, 0, 2)
+    else:
+        ko = torch.zeros((n, H, hs), dtype=torch.bfloat16, device="cuda")
+        vo = torch.zeros((n, H, hs), dtype=torch.bfloat16, device="cuda")
+    g.gather_upconvert_nvfp4_kv(cache5, ko, vo, dev(gcase.block_table), dev(gcase.workspace_starts),
+                                ks_d, vs_d, seq_starts=dev(gcase.seq_starts), layout=L_gpu)
+    torch.cuda.synchronize()
+    assert_same(host(ko.contiguous()), ok, "per-head gather K")
+    assert_same(host(vo.contiguous()), ov, "per-head gather V")
+
+
+def test_perhead_config5(g, orc):
+    w, _ = synth.config5()
+    L_orc = orc.kv_layout_split(w.block_size, 8, 128)
+    run_kv(orc, g, w.key, w.value, w.slot_mapping, w.num_blocks, w.block_size, L_orc, None,
+           w.k_scale, w.v_scale)
+
+
+@pytest.mark.parametrize("variant", ["interleaved", "hnd", "odd-head-size", "strided-input"])
+def test_perhead_layouts(g, orc, variant):
+    seed = {"interleaved": 41, "hnd": 42, "odd-head-size": 43, "strided-input": 44}[variant]
+    rng = np.random.default_rng(seed)
+    # head size 80: 5 scale blocks and 10 chunks per head (the non-power-of-two paths)
+    H, hs, nb, bs = (3, 80, 20, 16) if variant == "odd-head-size" else (4, 64, 16, 16)
+    T = 157
+    key, value, slots = _kv_case(rng, T, H, hs, nb, bs, 9)
+    ks, vs = synth.global_scale(key), synth.global_scale(value)
+    fd = hs // 2 + hs // 16
+    if variant == "interleaved":        # each (token, head) row is [data | scales]
+        kw = dict(data_offset=0, data_token_stride=H * fd, data_head_stride=fd, scale_offset=hs // 2,
+                  scale_token_stride=H * fd, scale_head_stride=fd, side_stride=bs * H * fd,
+                  block_stride=2 * bs * H * fd)
+    elif variant == "hnd":              # split layout with heads outermost inside a side
+        kw = dict(data_offset=0, data_token_stride=hs // 2, data_head_stride=bs * hs // 2,
+                  scale_offset=bs * H * hs // 2, scale_token_stride=hs // 16,
+                  scale_head_stride=bs * hs // 16, side_stride=bs * H * fd, block_stride=2 * bs * H * fd)
+    else:
+        kw = orc.kv_layout_split(bs, H, hs).as_dict()
+    L_orc, L_gpu = orc.KvLayout(**kw), g.NvFp4KvLayout(**kw)
+    kd = vd = None
+    if variant == "strided-input":      # key / value as slices of a wider [T, H, hs + 16] buffer
+        big = np.zeros((T, H, hs + 16), np.uint16)
+        big[:, :, :hs] = key
+        kd = dev(big)[:, :, :hs]
+        big2 = np.zeros((T, H, hs + 16), np.uint16)
+        big2[:, :, :hs] = value
+        vd = dev(big2)[:, :, :hs]
+    run_kv(orc, g, key, value, slots, nb, bs, L_orc, L_gpu, ks, vs, kd, vd, out_hnd=(variant == "hnd"))

@@ -195,11 +195,7 @@ def test_strided_inputs_and_padded_entries_vs_brute_force(orc):
     kv_c, k_pe = full[:, :512], full[:, 512:]
     slots = synth.padded_slots(rng, nb * bs, T, 5)
     cache = np.full(nb * bstr, 0x5A, np.uint8)
-    # strided views: pass the full buffer and the row stride through the C API
-    import ctypes as C
-    st = orc.lib().orc_write_nvfp4_ds_mla(full.ctypes.data, full[:, 512:].ctypes.data, cache.ctypes.data,
-                                          cache.size, slots.ctypes.data, T, 576, 576, nb, bs, bstr, es)
-    assert st == 0
+    orc.write_nvfp4_ds_mla(kv_c, k_pe, cache, slots, nb, bs, bstr, es)    # strided row views
     want = np.full_like(cache, 0x5A)
     brute.scatter(want, brute.nvfp4_ds_mla_entries(np.ascontiguousarray(kv_c), np.ascontiguousarray(k_pe)),
                   slots, bs, bstr, es)
