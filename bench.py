@@ -41,7 +41,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget-s", type=float, default=15.0,
+    ap.add_argument("--cpu-budget-s", type=float, default=20.0,
                     help="approximate CPU seconds for the oracle baseline sample")
     ap.add_argument("--cold", action="store_true",
                     help="also time every kernel once per run after evicting the caches")
@@ -250,59 +250,69 @@ def traffic_for(kernel):
 # ---------------------------------------------------------------------------
 def cpu_baseline(budget_s, w3, g3, w4, g4, w5, g5):
     """The oracle, as it stands, on a bounded sample of each workload, one
-    host thread.  Write samples: the first n tokens of each pre-fill; gather
-    samples: the first rows of each gather, reading a cache that holds the
-    oracle's own output for the sampled tokens (other entries zero; the
-    decode cost does not depend on the bytes).  GB/s from the same
-    algorithmic byte counts as the GPU figures."""
+    host thread.  Each op is first timed on a small slice to size its sample
+    to about budget_s / 6 seconds (capped at the whole workload).  Write
+    samples: the first n tokens of each pre-fill; gather samples: the first n
+    rows of each gather, reading a cache that holds the oracle's own output
+    for the sampled tokens (other entries zero; the decode cost does not
+    depend on the bytes).  GB/s from the same algorithmic byte counts as the
+    GPU figures."""
     import oracle
-    frac = budget_s / 15.0
-    n3, n4, n5 = int(16384 * frac), int(16384 * frac), int(1024 * frac)
-    r3, r4 = int(16384 * frac), int(16384 * frac)
-    res, tot_bytes, tot_s = {}, 0, 0.0
-
-    def timed(name, nbytes, fn):
-        nonlocal tot_bytes, tot_s
-        t = time.perf_counter()
-        fn()
-        s = time.perf_counter() - t
-        res[name] = {"s": round(s, 3), "GB_per_s": round(nbytes / s / 1e9, 4)}
-        tot_bytes += nbytes
-        tot_s += s
-
-    c3 = np.zeros(w3.num_blocks * w3.block_size * NV, np.uint8)
-    timed("nvfp4_ds_mla_write", n3 * (1152 + NV + 8),
-          lambda: oracle.write_nvfp4_ds_mla(w3.kv_c[:n3], w3.k_pe[:n3], c3, w3.slot_mapping[:n3],
-                                            w3.num_blocks, w3.block_size))
-    timed("nvfp4_ds_mla_gather", r3 * (NV + 1152),
-          lambda: oracle.gather_nvfp4_ds_mla(c3, r3, g3.block_table, g3.workspace_starts, g3.seq_starts,
-                                             g3.num_blocks, g3.block_size))
-    del c3
-    c4 = np.zeros(w4.num_blocks * w4.block_size * F8, np.uint8)
-    timed("fp8_ds_mla_write", n4 * (1152 + F8 + 8),
-          lambda: oracle.write_fp8_ds_mla(w4.kv_c[:n4], w4.k_pe[:n4], c4, w4.slot_mapping[:n4],
-                                          w4.num_blocks, w4.block_size))
-    timed("fp8_ds_mla_gather", r4 * (F8 + 1152),
-          lambda: oracle.gather_fp8_ds_mla(c4, r4, g4.block_table, g4.workspace_starts, g4.seq_starts,
-                                           g4.num_blocks, g4.block_size))
-    del c4
+    per_op = budget_s / 6.0
     H, hs = w5.key.shape[1], w5.key.shape[2]
     L = oracle.kv_layout_split(w5.block_size, H, hs)
+    c3 = np.zeros(w3.num_blocks * w3.block_size * NV, np.uint8)
+    c4 = np.zeros(w4.num_blocks * w4.block_size * F8, np.uint8)
     c5 = np.zeros(w5.num_blocks * L.block_stride, np.uint8)
-    sl = w5.slot_mapping[:n5]
-    timed("nvfp4_kv_write", int((sl >= 0).sum()) * 5248 + n5 * 8,
-          lambda: oracle.reshape_and_cache_nvfp4(np.ascontiguousarray(w5.key[:n5]),
-                                                 np.ascontiguousarray(w5.value[:n5]), c5, sl, w5.num_blocks,
-                                                 w5.block_size, L, w5.k_scale, w5.v_scale))
-    r5 = min(n5, g5.total_tokens)
-    timed("nvfp4_kv_gather", r5 * 5248,
-          lambda: oracle.gather_upconvert_nvfp4_kv(c5, r5, g5.block_table, g5.workspace_starts, g5.seq_starts,
-                                                   H, hs, w5.num_blocks, w5.block_size, L, w5.k_scale,
-                                                   w5.v_scale))
+
+    def kv_write(n):
+        sl = w5.slot_mapping[:n]
+        oracle.reshape_and_cache_nvfp4(np.ascontiguousarray(w5.key[:n]), np.ascontiguousarray(w5.value[:n]),
+                                       c5, sl, w5.num_blocks, w5.block_size, L, w5.k_scale, w5.v_scale)
+        return int((sl >= 0).sum()) * 2 * H * (2 * hs + hs // 2 + hs // 16) + n * 8
+
+    plan = [  # name, units available, run(n) -> algorithmic bytes
+        ("nvfp4_ds_mla_write", w3.num_tokens,
+         lambda n: (oracle.write_nvfp4_ds_mla(w3.kv_c[:n], w3.k_pe[:n], c3, w3.slot_mapping[:n],
+                                              w3.num_blocks, w3.block_size), n * (1152 + NV + 8))[1]),
+        ("nvfp4_ds_mla_gather", g3.total_tokens,
+         lambda n: (oracle.gather_nvfp4_ds_mla(c3, n, g3.block_table, g3.workspace_starts, g3.seq_starts,
+                                               g3.num_blocks, g3.block_size), n * (NV + 1152))[1]),
+        ("fp8_ds_mla_write", w4.num_tokens,
+         lambda n: (oracle.write_fp8_ds_mla(w4.kv_c[:n], w4.k_pe[:n], c4, w4.slot_mapping[:n],
+                                            w4.num_blocks, w4.block_size), n * (1152 + F8 + 8))[1]),
+        ("fp8_ds_mla_gather", g4.total_tokens,
+         lambda n: (oracle.gather_fp8_ds_mla(c4, n, g4.block_table, g4.workspace_starts, g4.seq_starts,
+                                             g4.num_blocks, g4.block_size), n * (F8 + 1152))[1]),
+        ("nvfp4_kv_write", w5.slot_mapping.shape[0], kv_write),
+        ("nvfp4_kv_gather", g5.total_tokens,
+         lambda n: (oracle.gather_upconvert_nvfp4_kv(c5, n, g5.block_table, g5.workspace_starts,
+                                                     g5.seq_starts, H, hs, w5.num_blocks, w5.block_size, L,
+                                                     w5.k_scale, w5.v_scale), n * 2 * H * (2 * hs + hs // 2 + hs // 16))[1]),
+    ]
+    res, tot_bytes, tot_s, desc = {}, 0, 0.0, []
+    for name, avail, run in plan:
+        n0 = min(avail, 64)
+        while True:                              # calibrate on >= 0.1 s of work
+            t = time.perf_counter()
+            run(n0)
+            el = time.perf_counter() - t
+            if el >= 0.1 or n0 >= avail:
+                break
+            n0 = min(avail, n0 * 4)
+        per_unit = max(el / n0, 1e-9)
+        n = int(min(avail, max(n0, per_op / per_unit)))
+        t = time.perf_counter()
+        nbytes = run(n)
+        sec = time.perf_counter() - t
+        res[name] = {"units": n, "s": round(sec, 3), "GB_per_s": round(nbytes / sec / 1e9, 4)}
+        tot_bytes += nbytes
+        tot_s += sec
+        desc.append(f"{name} {n}/{avail}")
     return {"value": round(tot_bytes / tot_s / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {n3} / {n4} tokens of the nvfp4 / fp8 pre-fill writes, first {r3} / {r4} rows "
-                      f"of the nvfp4 / fp8 gathers, first {n5} tokens of the per-head write and {r5} rows "
-                      f"of its gather; single-threaded C oracle (-O2), {tot_s:.1f} s in total",
+            "sample": "first units of each op's full workload (" + ", ".join(desc) + "); write samples "
+                      "take the first tokens, gather samples the first workspace rows; single-threaded "
+                      f"C oracle (gcc -O2), {tot_s:.1f} s of CPU time",
             "per_op": res, "host_cpu": _cpu_name()}
 
 
