@@ -6,19 +6,20 @@
 // kernel excerpts under "Key source excerpts"); the gather walk with
 // seq_starts: vLLM PR #48642 digest ("Implementation breakdown" item 2).
 //
-// All four kernels are HBM-bound streams with no contraction.  Mapping:
+// All four kernels are HBM-bound streams with no contraction.  What bounds
+// them on MI355X is latency (bytes in flight) and the cache state left by
+// the previous op, so every wave issues all of its loads before it needs
+// them, and inputs/outputs use streaming (nontemporal) accesses.
 //   nvfp4 write : one lane per 16-value NoPE block (32 B in, 8 B + 1 scale
-//                 byte out), so a wave covers two tokens and needs no
-//                 cross-lane reduction; the block's amax, scale and
-//                 reciprocal are computed once per lane.
-//   fp8 write   : one wave per token, 8 values per lane (one 16 B load);
-//                 the 128-value group amax is a 4-step DPP butterfly inside
-//                 each 16-lane row.
-//   gathers     : one wave per 16 workspace rows; lanes 0..15 resolve the
-//                 rows' cache addresses in parallel (binary search over
-//                 workspace_starts, one block-table load), then every row is
-//                 read and written with whole-wave contiguous accesses
-//                 (NoPE: 4 or 8 B per lane in, 16 B per lane out).
+//                 byte out), two tokens per half-wave pair, four tokens per
+//                 wave; no cross-lane reduction.
+//   fp8 write   : 8 values per lane (one 16 B load), a token per wave-row of
+//                 64 lanes, four tokens per wave; the 128-value group amax is
+//                 a 4-step DPP butterfly inside each 16-lane row.
+//   gathers     : 8 workspace rows per wave; lanes 0..7 resolve the rows'
+//                 cache addresses (binary search over workspace_starts staged
+//                 in LDS, one block-table load), then each row is read and
+//                 written by the whole wave with contiguous accesses.
 #include "gcache_internal.h"
 
 namespace gcache {
@@ -26,63 +27,82 @@ namespace gcache {
 // ---------------------------------------------------------------------------
 // nvfp4_ds_mla write
 // ---------------------------------------------------------------------------
+constexpr int kNvTokPerWave = 4;   // two half-wave pairs
+
+__device__ __forceinline__ void nv_quantize_store(const DsMlaWriteParams& p, int64_t slot, uint4 v0,
+                                                  uint4 v1, uint32_t rw, int j) {
+    const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    float x[16];
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+        x[2 * k] = bf16_lo(w[k]);
+        x[2 * k + 1] = bf16_hi(w[k]);
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 16; k++) amax = fmaxf(amax, fabsf(x[k]));
+
+    // Block scale: e4m3_rn_sat(amax / 6), then the binary32 reciprocal of
+    // its decoded value (0 for a zero scale).
+    const uint32_t sf = put_e4m3x2<false>(0u, amax / 6.0f, 0.0f) & 0xFFu;
+    const float s = e4m3_f32(sf);
+    const float inv = (s == 0.0f) ? 0.0f : 1.0f / s;
+
+    uint32_t q0 = 0, q1 = 0;
+    q0 = put_e2m1x2<0>(q0, x[0] * inv, x[1] * inv);
+    q0 = put_e2m1x2<1>(q0, x[2] * inv, x[3] * inv);
+    q0 = put_e2m1x2<2>(q0, x[4] * inv, x[5] * inv);
+    q0 = put_e2m1x2<3>(q0, x[6] * inv, x[7] * inv);
+    q1 = put_e2m1x2<0>(q1, x[8] * inv, x[9] * inv);
+    q1 = put_e2m1x2<1>(q1, x[10] * inv, x[11] * inv);
+    q1 = put_e2m1x2<2>(q1, x[12] * inv, x[13] * inv);
+    q1 = put_e2m1x2<3>(q1, x[14] * inv, x[15] * inv);
+    const uint32_t rq = put_e4m3x2<false>(0u, bf16_lo(rw), bf16_hi(rw));
+
+    int64_t blk, off;
+    split_block(slot, p.div, blk, off);
+    uint8_t* e = p.cache + blk * p.block_stride + off * p.entry_stride;
+    st_stream8(e + 8 * j, make_uint2(q0, q1));
+    st_stream2(e + kNvRopeOff + 2 * j, (uint16_t)rq);
+    st_stream1(e + kNvScaleOff + j, (uint8_t)sf);
+}
+
 __global__ __launch_bounds__(kBlockThreads) void k_write_nvfp4_ds_mla(DsMlaWriteParams p) {
     const int lane = lane_id();
     const int half = lane >> 5;   // token of the pair
     const int j = lane & 31;      // NoPE block (values 16j .. 16j+15), RoPE pair j
-    const int64_t npairs = (p.num_tokens + 1) >> 1;
+    const int64_t ngroups = (p.num_tokens + kNvTokPerWave - 1) / kNvTokPerWave;
     const int64_t step = (int64_t)gridDim.x * kWavesPerBlock;
-    for (int64_t pair = (int64_t)blockIdx.x * kWavesPerBlock + wave_id(); pair < npairs;
-         pair += step) {
-        const int64_t t = 2 * pair + half;
-        if (t >= p.num_tokens) continue;
-        const int64_t slot = p.slots[t];
-        if (slot < 0) continue;                               // padding token
-
-        const uint4* src = reinterpret_cast<const uint4*>(p.kv_c + t * p.kv_c_stride) + 2 * j;
-        const uint4 v0 = src[0], v1 = src[1];
-        const uint32_t rw = reinterpret_cast<const uint32_t*>(p.k_pe + t * p.k_pe_stride)[j];
-
-        const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-        float x[16];
+    for (int64_t g = (int64_t)blockIdx.x * kWavesPerBlock + wave_id(); g < ngroups; g += step) {
+        int64_t slot[2];
+        uint4 v0[2], v1[2];
+        uint32_t rw[2];
 #pragma unroll
-        for (int k = 0; k < 8; k++) {
-            x[2 * k] = bf16_lo(w[k]);
-            x[2 * k + 1] = bf16_hi(w[k]);
+        for (int k = 0; k < 2; k++) {
+            const int64_t t = g * kNvTokPerWave + 2 * k + half;
+            slot[k] = (t < p.num_tokens) ? p.slots[t] : -1;
         }
-        float amax = 0.0f;
 #pragma unroll
-        for (int k = 0; k < 16; k++) amax = fmaxf(amax, fabsf(x[k]));
-
-        // Block scale: e4m3_rn_sat(amax / 6), then the binary32 reciprocal of
-        // its decoded value (0 for a zero scale).
-        const uint32_t sf = put_e4m3x2<false>(0u, amax / 6.0f, 0.0f) & 0xFFu;
-        const float s = e4m3_f32(sf);
-        const float inv = (s == 0.0f) ? 0.0f : 1.0f / s;
-
-        uint32_t q0 = 0, q1 = 0;
-        q0 = put_e2m1x2<0>(q0, x[0] * inv, x[1] * inv);
-        q0 = put_e2m1x2<1>(q0, x[2] * inv, x[3] * inv);
-        q0 = put_e2m1x2<2>(q0, x[4] * inv, x[5] * inv);
-        q0 = put_e2m1x2<3>(q0, x[6] * inv, x[7] * inv);
-        q1 = put_e2m1x2<0>(q1, x[8] * inv, x[9] * inv);
-        q1 = put_e2m1x2<1>(q1, x[10] * inv, x[11] * inv);
-        q1 = put_e2m1x2<2>(q1, x[12] * inv, x[13] * inv);
-        q1 = put_e2m1x2<3>(q1, x[14] * inv, x[15] * inv);
-        const uint32_t rq = put_e4m3x2<false>(0u, bf16_lo(rw), bf16_hi(rw));
-
-        int64_t blk, off;
-        split_block(slot, p.div, blk, off);
-        uint8_t* e = p.cache + blk * p.block_stride + off * p.entry_stride;
-        *reinterpret_cast<uint2*>(e + 8 * j) = make_uint2(q0, q1);
-        *reinterpret_cast<uint16_t*>(e + kNvRopeOff + 2 * j) = (uint16_t)rq;
-        e[kNvScaleOff + j] = (uint8_t)sf;
+        for (int k = 0; k < 2; k++) {                    // padding tokens read nothing
+            if (slot[k] >= 0) {
+                const int64_t t = g * kNvTokPerWave + 2 * k + half;
+                const uint8_t* row = reinterpret_cast<const uint8_t*>(p.kv_c + t * p.kv_c_stride) + 32 * j;
+                v0[k] = ld_stream16(row);
+                v1[k] = ld_stream16(row + 16);
+                rw[k] = ld_stream4(reinterpret_cast<const uint8_t*>(p.k_pe + t * p.k_pe_stride) + 4 * j);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < 2; k++)
+            if (slot[k] >= 0) nv_quantize_store(p, slot[k], v0[k], v1[k], rw[k], j);
     }
 }
 
 // ---------------------------------------------------------------------------
 // fp8_ds_mla write: 512 e4m3 | 4 x fp32 scale (amax / 448 per 128) | 64 bf16
 // ---------------------------------------------------------------------------
+constexpr int kF8TokPerWave = 4;
+
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float v) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
@@ -90,45 +110,63 @@ __device__ __forceinline__ float dpp_f32(float v) {
 
 __global__ __launch_bounds__(kBlockThreads) void k_write_fp8_ds_mla(DsMlaWriteParams p) {
     const int lane = lane_id();
+    const int64_t ngroups = (p.num_tokens + kF8TokPerWave - 1) / kF8TokPerWave;
     const int64_t step = (int64_t)gridDim.x * kWavesPerBlock;
-    for (int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + wave_id(); t < p.num_tokens;
-         t += step) {
-        const int64_t slot = p.slots[t];
-        if (slot < 0) continue;                               // wave-uniform
-
-        const uint4 v = reinterpret_cast<const uint4*>(p.kv_c + t * p.kv_c_stride)[lane];
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-        float x[8];
+    for (int64_t g = (int64_t)blockIdx.x * kWavesPerBlock + wave_id(); g < ngroups; g += step) {
+        const int64_t t0 = g * kF8TokPerWave;
+        int64_t slot[kF8TokPerWave];                     // wave-uniform
 #pragma unroll
-        for (int k = 0; k < 4; k++) {
-            x[2 * k] = bf16_lo(w[k]);
-            x[2 * k + 1] = bf16_hi(w[k]);
+        for (int k = 0; k < kF8TokPerWave; k++)
+            slot[k] = (t0 + k < p.num_tokens) ? p.slots[t0 + k] : -1;
+        uint4 v[kF8TokPerWave];
+#pragma unroll
+        for (int k = 0; k < kF8TokPerWave; k++)
+            if (slot[k] >= 0)
+                v[k] = ld_stream16(reinterpret_cast<const uint8_t*>(p.kv_c + (t0 + k) * p.kv_c_stride) + 16 * lane);
+        // RoPE (128 B bf16 per token): lanes 0..31, 8 lanes x 16 B per token.
+        const int rk = (lane >> 3) & 3, rc = lane & 7;
+        const int64_t rslot = rk == 0 ? slot[0] : rk == 1 ? slot[1] : rk == 2 ? slot[2] : slot[3];
+        uint4 r = make_uint4(0, 0, 0, 0);
+        if (lane < 32 && rslot >= 0)
+            r = ld_stream16(reinterpret_cast<const uint8_t*>(p.k_pe + (t0 + rk) * p.k_pe_stride) + 16 * rc);
+
+#pragma unroll
+        for (int k = 0; k < kF8TokPerWave; k++) {
+            if (slot[k] < 0) continue;                   // wave-uniform: DPP below sees all lanes
+            const uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+            float x[8];
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                x[2 * i] = bf16_lo(w[i]);
+                x[2 * i + 1] = bf16_hi(w[i]);
+            }
+            float amax = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; i++) amax = fmaxf(amax, fabsf(x[i]));
+            // 16 lanes x 8 values = one 128-value group: butterfly max in the row.
+            amax = fmaxf(amax, dpp_f32<0xB1>(amax));    // quad_perm [1,0,3,2]
+            amax = fmaxf(amax, dpp_f32<0x4E>(amax));    // quad_perm [2,3,0,1]
+            amax = fmaxf(amax, dpp_f32<0x141>(amax));   // row_half_mirror
+            amax = fmaxf(amax, dpp_f32<0x140>(amax));   // row_mirror
+
+            const float sc = amax / 448.0f;
+            const float inv = (sc == 0.0f) ? 0.0f : 1.0f / sc;
+            uint32_t q0 = 0, q1 = 0;
+            q0 = put_e4m3x2<false>(q0, x[0] * inv, x[1] * inv);
+            q0 = put_e4m3x2<true>(q0, x[2] * inv, x[3] * inv);
+            q1 = put_e4m3x2<false>(q1, x[4] * inv, x[5] * inv);
+            q1 = put_e4m3x2<true>(q1, x[6] * inv, x[7] * inv);
+
+            int64_t blk, off;
+            split_block(slot[k], p.div, blk, off);
+            uint8_t* e = p.cache + blk * p.block_stride + off * p.entry_stride;
+            st_stream8(e + 8 * lane, make_uint2(q0, q1));
+            if ((lane & 15) == 0) st_stream4(e + kF8ScaleOff + 4 * (lane >> 4), __float_as_uint(sc));
         }
-        float amax = 0.0f;
-#pragma unroll
-        for (int k = 0; k < 8; k++) amax = fmaxf(amax, fabsf(x[k]));
-        // 16 lanes x 8 values = one 128-value group: butterfly max in the row.
-        amax = fmaxf(amax, dpp_f32<0xB1>(amax));    // quad_perm [1,0,3,2]
-        amax = fmaxf(amax, dpp_f32<0x4E>(amax));    // quad_perm [2,3,0,1]
-        amax = fmaxf(amax, dpp_f32<0x141>(amax));   // row_half_mirror
-        amax = fmaxf(amax, dpp_f32<0x140>(amax));   // row_mirror
-
-        const float sc = amax / 448.0f;
-        const float inv = (sc == 0.0f) ? 0.0f : 1.0f / sc;
-        uint32_t q0 = 0, q1 = 0;
-        q0 = put_e4m3x2<false>(q0, x[0] * inv, x[1] * inv);
-        q0 = put_e4m3x2<true>(q0, x[2] * inv, x[3] * inv);
-        q1 = put_e4m3x2<false>(q1, x[4] * inv, x[5] * inv);
-        q1 = put_e4m3x2<true>(q1, x[6] * inv, x[7] * inv);
-
-        int64_t blk, off;
-        split_block(slot, p.div, blk, off);
-        uint8_t* e = p.cache + blk * p.block_stride + off * p.entry_stride;
-        reinterpret_cast<uint2*>(e)[lane] = make_uint2(q0, q1);
-        if ((lane & 15) == 0) reinterpret_cast<float*>(e + kF8ScaleOff)[lane >> 4] = sc;
-        if (lane < 8) {
-            const uint4 r = reinterpret_cast<const uint4*>(p.k_pe + t * p.k_pe_stride)[lane];
-            reinterpret_cast<uint4*>(e + kF8RopeOff)[lane] = r;
+        if (lane < 32 && rslot >= 0) {
+            int64_t blk, off;
+            split_block(rslot, p.div, blk, off);
+            st_stream16(p.cache + blk * p.block_stride + off * p.entry_stride + kF8RopeOff + 16 * rc, r);
         }
     }
 }
@@ -136,12 +174,25 @@ __global__ __launch_bounds__(kBlockThreads) void k_write_fp8_ds_mla(DsMlaWritePa
 // ---------------------------------------------------------------------------
 // gathers
 // ---------------------------------------------------------------------------
-constexpr int kRowsPerWave = 16;
+constexpr int kRowsPerWave = 8;
+constexpr int kWalkLds = 1024;     // workspace_starts / seq_starts staged in LDS up to this batch
 
-// Cache byte offset of the entry read by workspace row r.
-__device__ __forceinline__ int64_t row_entry_offset(const DsMlaGatherParams& p, int64_t r) {
-    const int b = find_request(p.ws, p.batch, r);
-    const int64_t pos = (p.seq_starts ? (int64_t)p.seq_starts[b] : 0) + (r - (int64_t)p.ws[b]);
+// Cache byte offset of the entry read by workspace row r; the request search
+// runs over the LDS copy when the batch fits, else over global memory.
+__device__ __forceinline__ int64_t row_entry_offset(const DsMlaGatherParams& p, const int32_t* s_ws,
+                                                    const int32_t* s_ss, bool lds, int64_t r) {
+    int b;
+    int64_t wsb, ssb;
+    if (lds) {
+        b = find_request(s_ws, p.batch, r);
+        wsb = s_ws[b];
+        ssb = s_ss[b];
+    } else {
+        b = find_request(p.ws, p.batch, r);
+        wsb = p.ws[b];
+        ssb = p.seq_starts ? p.seq_starts[b] : 0;
+    }
+    const int64_t pos = ssb + (r - wsb);
     int64_t bi, off;
     split_block(pos, p.div, bi, off);
     const int64_t blk = p.block_table[(int64_t)b * p.bt_stride + bi];
@@ -161,6 +212,15 @@ __device__ __forceinline__ int64_t shfl64(int64_t v, int src_lane) {
 
 template <bool NVFP4>
 __global__ __launch_bounds__(kBlockThreads) void k_gather_ds_mla(DsMlaGatherParams p) {
+    __shared__ int32_t s_ws[kWalkLds], s_ss[kWalkLds];
+    const bool lds = p.batch <= kWalkLds;
+    if (lds) {
+        for (int i = threadIdx.x; i < p.batch; i += kBlockThreads) {
+            s_ws[i] = p.ws[i];
+            s_ss[i] = p.seq_starts ? p.seq_starts[i] : 0;
+        }
+        __syncthreads();
+    }
     const int lane = lane_id();
     const int64_t ngroups = (p.total + kRowsPerWave - 1) / kRowsPerWave;
     const int64_t step = (int64_t)gridDim.x * kWavesPerBlock;
@@ -168,52 +228,67 @@ __global__ __launch_bounds__(kBlockThreads) void k_gather_ds_mla(DsMlaGatherPara
         const int64_t r0 = g * kRowsPerWave;
         const int nrows = (int)min((int64_t)kRowsPerWave, p.total - r0);
         int64_t eoff = 0;
-        if (lane < nrows) eoff = row_entry_offset(p, r0 + lane);
+        if (lane < nrows) eoff = row_entry_offset(p, s_ws, s_ss, lds, r0 + lane);
 
-        // NoPE: one row per iteration, the whole wave on one entry.
+        // Issue every load of the 8 rows first, then convert and store.
+        uint32_t a32[kRowsPerWave];      // nvfp4: 8 codes; fp8: scale bits
+        uint2 a64[kRowsPerWave];         // fp8: 8 codes
 #pragma unroll
         for (int k = 0; k < kRowsPerWave; k++) {
             if (k >= nrows) continue;
             const uint8_t* e = p.cache + readlane64(eoff, k);
+            if (NVFP4) {
+                a32[k] = ld_stream4(e + 4 * lane);                             // values 8l..8l+7
+                a64[k].x = ld_stream1(e + kNvScaleOff + (lane >> 1));          // their scale
+            } else {
+                a64[k] = ld_stream8(e + 8 * lane);                             // codes 8l..8l+7
+                a32[k] = ld_stream4(e + kF8ScaleOff + 4 * (lane >> 4));        // group scale
+            }
+        }
+        // RoPE: lane -> row lane/8, 8 values (16 B out) per lane.
+        const int rk = lane >> 3, rc = lane & 7;
+        const int64_t reo = shfl64(eoff, rk);
+        uint4 rv = make_uint4(0, 0, 0, 0);
+        if (rk < nrows) {
+            const uint8_t* e = p.cache + reo;
+            if (NVFP4) {
+                const uint2 q = ld_stream8(e + kNvRopeOff + 8 * rc);
+                rv.x = q.x;
+                rv.y = q.y;
+            } else {
+                rv = ld_stream16(e + kF8RopeOff + 16 * rc);
+            }
+        }
+
+#pragma unroll
+        for (int k = 0; k < kRowsPerWave; k++) {
+            if (k >= nrows) continue;
             uint4 o;
             if (NVFP4) {
-                const uint32_t nib = reinterpret_cast<const uint32_t*>(e)[lane];  // values 8l..8l+7
-                const float s = e4m3_f32(e[kNvScaleOff + (lane >> 1)]);
+                const uint32_t nib = a32[k];
+                const float s = e4m3_f32(a64[k].x);
                 const f32x2 a = e2m1x2_f32<0>(nib), b = e2m1x2_f32<1>(nib);
                 const f32x2 c = e2m1x2_f32<2>(nib), d = e2m1x2_f32<3>(nib);
                 o = make_uint4(pack_bf16x2(a.x * s, a.y * s), pack_bf16x2(b.x * s, b.y * s),
                                pack_bf16x2(c.x * s, c.y * s), pack_bf16x2(d.x * s, d.y * s));
             } else {
-                const uint2 q = reinterpret_cast<const uint2*>(e)[lane];          // codes 8l..8l+7
-                const float sc = reinterpret_cast<const float*>(e + kF8ScaleOff)[lane >> 4];
-                const f32x2 a = e4m3x2_f32<false>(q.x), b = e4m3x2_f32<true>(q.x);
-                const f32x2 c = e4m3x2_f32<false>(q.y), d = e4m3x2_f32<true>(q.y);
+                const float sc = __uint_as_float(a32[k]);
+                const f32x2 a = e4m3x2_f32<false>(a64[k].x), b = e4m3x2_f32<true>(a64[k].x);
+                const f32x2 c = e4m3x2_f32<false>(a64[k].y), d = e4m3x2_f32<true>(a64[k].y);
                 o = make_uint4(pack_bf16x2(a.x * sc, a.y * sc), pack_bf16x2(b.x * sc, b.y * sc),
                                pack_bf16x2(c.x * sc, c.y * sc), pack_bf16x2(d.x * sc, d.y * sc));
             }
-            reinterpret_cast<uint4*>(p.dst + (r0 + k) * p.dst_stride)[lane] = o;
+            st_stream16(p.dst + (r0 + k) * p.dst_stride + 8 * lane, o);
         }
-
-        // RoPE: 8 rows per pass, 8 lanes per row, 8 values (16 B out) per lane.
-#pragma unroll
-        for (int h = 0; h < kRowsPerWave / 8; h++) {
-            const int k = 8 * h + (lane >> 3);
-            const int c = lane & 7;
-            const int64_t eo = shfl64(eoff, k);
-            if (k < nrows) {
-                const uint8_t* e = p.cache + eo;
-                uint4 o;
-                if (NVFP4) {
-                    const uint2 q = reinterpret_cast<const uint2*>(e + kNvRopeOff)[c];
-                    const f32x2 a = e4m3x2_f32<false>(q.x), b = e4m3x2_f32<true>(q.x);
-                    const f32x2 cc = e4m3x2_f32<false>(q.y), d = e4m3x2_f32<true>(q.y);
-                    o = make_uint4(pack_bf16x2(a.x, a.y), pack_bf16x2(b.x, b.y),
-                                   pack_bf16x2(cc.x, cc.y), pack_bf16x2(d.x, d.y));
-                } else {
-                    o = reinterpret_cast<const uint4*>(e + kF8RopeOff)[c];
-                }
-                reinterpret_cast<uint4*>(p.dst + (r0 + k) * p.dst_stride + kNope)[c] = o;
+        if (rk < nrows) {
+            uint4 o = rv;
+            if (NVFP4) {
+                const f32x2 a = e4m3x2_f32<false>(rv.x), b = e4m3x2_f32<true>(rv.x);
+                const f32x2 c = e4m3x2_f32<false>(rv.y), d = e4m3x2_f32<true>(rv.y);
+                o = make_uint4(pack_bf16x2(a.x, a.y), pack_bf16x2(b.x, b.y), pack_bf16x2(c.x, c.y),
+                               pack_bf16x2(d.x, d.y));
             }
+            st_stream16(p.dst + (r0 + rk) * p.dst_stride + kNope + 8 * rc, o);
         }
     }
 }
@@ -222,10 +297,10 @@ __global__ __launch_bounds__(kBlockThreads) void k_gather_ds_mla(DsMlaGatherPara
 // launchers
 // ---------------------------------------------------------------------------
 hipError_t launch_write_nvfp4_ds_mla(const DsMlaWriteParams& p, hipStream_t s) {
-    return launch1(k_write_nvfp4_ds_mla, grid_for_waves((p.num_tokens + 1) / 2), s, p);
+    return launch1(k_write_nvfp4_ds_mla, grid_for_waves((p.num_tokens + kNvTokPerWave - 1) / kNvTokPerWave), s, p);
 }
 hipError_t launch_write_fp8_ds_mla(const DsMlaWriteParams& p, hipStream_t s) {
-    return launch1(k_write_fp8_ds_mla, grid_for_waves(p.num_tokens), s, p);
+    return launch1(k_write_fp8_ds_mla, grid_for_waves((p.num_tokens + kF8TokPerWave - 1) / kF8TokPerWave), s, p);
 }
 hipError_t launch_gather_nvfp4_ds_mla(const DsMlaGatherParams& p, hipStream_t s) {
     return launch1(k_gather_ds_mla<true>,

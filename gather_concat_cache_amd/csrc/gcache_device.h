@@ -87,6 +87,47 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
+// Streaming accesses.  Every input byte of these kernels is read once and
+// every output byte written once, so loads and stores carry the nontemporal
+// hint: in the dirty-cache state a pipeline of such ops runs in, this keeps
+// the streams from evicting (and writing back) lines in the 256 MB
+// last-level cache and L2, which measured +15-25% on the gathers and the
+// writes.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint4 ld_stream16(const void* p) {
+    const u32x4 v = __builtin_nontemporal_load(static_cast<const u32x4*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 ld_stream8(const void* p) {
+    const u32x2 v = __builtin_nontemporal_load(static_cast<const u32x2*>(p));
+    return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ uint32_t ld_stream4(const void* p) {
+    return __builtin_nontemporal_load(static_cast<const uint32_t*>(p));
+}
+__device__ __forceinline__ uint32_t ld_stream1(const void* p) {
+    return __builtin_nontemporal_load(static_cast<const uint8_t*>(p));
+}
+__device__ __forceinline__ void st_stream16(void* p, uint4 v) {
+    const u32x4 w = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(w, static_cast<u32x4*>(p));
+}
+__device__ __forceinline__ void st_stream8(void* p, uint2 v) {
+    const u32x2 w = {v.x, v.y};
+    __builtin_nontemporal_store(w, static_cast<u32x2*>(p));
+}
+__device__ __forceinline__ void st_stream4(void* p, uint32_t v) {
+    __builtin_nontemporal_store(v, static_cast<uint32_t*>(p));
+}
+__device__ __forceinline__ void st_stream2(void* p, uint16_t v) {
+    __builtin_nontemporal_store(v, static_cast<uint16_t*>(p));
+}
+__device__ __forceinline__ void st_stream1(void* p, uint8_t v) {
+    __builtin_nontemporal_store(v, static_cast<uint8_t*>(p));
+}
+
 // Split a slot (or logical position) into (block, offset).  `shift` >= 0
 // when block_size is a power of two.
 struct BlockDiv {
