@@ -7,19 +7,25 @@
 // seq_starts: vLLM PR #48642 digest ("Implementation breakdown" item 2).
 //
 // All four kernels are HBM-bound streams with no contraction.  What bounds
-// them on MI355X is latency (bytes in flight) and the cache state left by
-// the previous op, so every wave issues all of its loads before it needs
-// them, and inputs/outputs use streaming (nontemporal) accesses.
+// them on MI355X is latency (bytes in flight), the cache state left by the
+// previous op and the spread of the write front, so:
+//   - every wave is one-shot (one small group of tokens or rows, no
+//     grid-stride loop): the waves in flight then cover a compact, advancing
+//     window of addresses, which the memory system writes far faster than
+//     the scattered fronts of persistent loops;
+//   - every wave issues all of its loads before it needs them;
+//   - inputs and outputs use streaming (nontemporal) accesses.
+// Mappings:
 //   nvfp4 write : one lane per 16-value NoPE block (32 B in, 8 B + 1 scale
 //                 byte out), two tokens per half-wave pair, four tokens per
 //                 wave; no cross-lane reduction.
-//   fp8 write   : 8 values per lane (one 16 B load), a token per wave-row of
-//                 64 lanes, four tokens per wave; the 128-value group amax is
-//                 a 4-step DPP butterfly inside each 16-lane row.
-//   gathers     : 8 workspace rows per wave; lanes 0..7 resolve the rows'
-//                 cache addresses (binary search over workspace_starts staged
-//                 in LDS, one block-table load), then each row is read and
-//                 written by the whole wave with contiguous accesses.
+//   fp8 write   : 8 values per lane (one 16 B load), one token per 64 lanes,
+//                 two tokens per wave; the 128-value group amax is a 4-step
+//                 DPP butterfly inside each 16-lane row.
+//   gathers     : 4 workspace rows per wave; lanes 0..3 resolve the rows'
+//                 cache addresses (search over workspace_starts, one
+//                 block-table load), then each row is read and written by
+//                 the whole wave with contiguous accesses.
 #include "gcache_internal.h"
 
 namespace gcache {
@@ -67,132 +73,115 @@ __device__ __forceinline__ void nv_quantize_store(const DsMlaWriteParams& p, int
     st_stream1(e + kNvScaleOff + j, (uint8_t)sf);
 }
 
-__global__ __launch_bounds__(kBlockThreads) void k_write_nvfp4_ds_mla(DsMlaWriteParams p) {
+__global__ __launch_bounds__(kBlockThreads) void k_write_nvfp4_ds_mla(DsMlaWriteParams p, int64_t wave0) {
     const int lane = lane_id();
     const int half = lane >> 5;   // token of the pair
     const int j = lane & 31;      // NoPE block (values 16j .. 16j+15), RoPE pair j
-    const int64_t ngroups = (p.num_tokens + kNvTokPerWave - 1) / kNvTokPerWave;
-    const int64_t step = (int64_t)gridDim.x * kWavesPerBlock;
-    for (int64_t g = (int64_t)blockIdx.x * kWavesPerBlock + wave_id(); g < ngroups; g += step) {
-        int64_t slot[2];
-        uint4 v0[2], v1[2];
-        uint32_t rw[2];
+    const int64_t g = wave0 + (int64_t)blockIdx.x * kWavesPerBlock + wave_id();
+    if (g * kNvTokPerWave >= p.num_tokens) return;
+    int64_t slot[2];
+    uint4 v0[2], v1[2];
+    uint32_t rw[2];
 #pragma unroll
-        for (int k = 0; k < 2; k++) {
-            const int64_t t = g * kNvTokPerWave + 2 * k + half;
-            slot[k] = (t < p.num_tokens) ? p.slots[t] : -1;
-        }
-#pragma unroll
-        for (int k = 0; k < 2; k++) {                    // padding tokens read nothing
-            if (slot[k] >= 0) {
-                const int64_t t = g * kNvTokPerWave + 2 * k + half;
-                const uint8_t* row = reinterpret_cast<const uint8_t*>(p.kv_c + t * p.kv_c_stride) + 32 * j;
-                v0[k] = ld_stream16(row);
-                v1[k] = ld_stream16(row + 16);
-                rw[k] = ld_stream4(reinterpret_cast<const uint8_t*>(p.k_pe + t * p.k_pe_stride) + 4 * j);
-            }
-        }
-#pragma unroll
-        for (int k = 0; k < 2; k++)
-            if (slot[k] >= 0) nv_quantize_store(p, slot[k], v0[k], v1[k], rw[k], j);
+    for (int k = 0; k < 2; k++) {
+        const int64_t t = g * kNvTokPerWave + 2 * k + half;
+        slot[k] = (t < p.num_tokens) ? p.slots[t] : -1;
     }
+#pragma unroll
+    for (int k = 0; k < 2; k++) {                        // padding tokens read nothing
+        if (slot[k] >= 0) {
+            const int64_t t = g * kNvTokPerWave + 2 * k + half;
+            const uint8_t* row = reinterpret_cast<const uint8_t*>(p.kv_c + t * p.kv_c_stride) + 32 * j;
+            v0[k] = ld_stream16(row);
+            v1[k] = ld_stream16(row + 16);
+            rw[k] = ld_stream4(reinterpret_cast<const uint8_t*>(p.k_pe + t * p.k_pe_stride) + 4 * j);
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < 2; k++)
+        if (slot[k] >= 0) nv_quantize_store(p, slot[k], v0[k], v1[k], rw[k], j);
 }
 
 // ---------------------------------------------------------------------------
 // fp8_ds_mla write: 512 e4m3 | 4 x fp32 scale (amax / 448 per 128) | 64 bf16
 // ---------------------------------------------------------------------------
-constexpr int kF8TokPerWave = 4;
+constexpr int kF8TokPerWave = 2;
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float v) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 
-__global__ __launch_bounds__(kBlockThreads) void k_write_fp8_ds_mla(DsMlaWriteParams p) {
+__global__ __launch_bounds__(kBlockThreads) void k_write_fp8_ds_mla(DsMlaWriteParams p, int64_t wave0) {
     const int lane = lane_id();
-    const int64_t ngroups = (p.num_tokens + kF8TokPerWave - 1) / kF8TokPerWave;
-    const int64_t step = (int64_t)gridDim.x * kWavesPerBlock;
-    for (int64_t g = (int64_t)blockIdx.x * kWavesPerBlock + wave_id(); g < ngroups; g += step) {
-        const int64_t t0 = g * kF8TokPerWave;
-        int64_t slot[kF8TokPerWave];                     // wave-uniform
+    const int64_t t0 = (wave0 + (int64_t)blockIdx.x * kWavesPerBlock + wave_id()) * kF8TokPerWave;
+    if (t0 >= p.num_tokens) return;
+    int64_t slot[kF8TokPerWave];                         // wave-uniform
 #pragma unroll
-        for (int k = 0; k < kF8TokPerWave; k++)
-            slot[k] = (t0 + k < p.num_tokens) ? p.slots[t0 + k] : -1;
-        uint4 v[kF8TokPerWave];
+    for (int k = 0; k < kF8TokPerWave; k++)
+        slot[k] = (t0 + k < p.num_tokens) ? p.slots[t0 + k] : -1;
+    uint4 v[kF8TokPerWave];
 #pragma unroll
-        for (int k = 0; k < kF8TokPerWave; k++)
-            if (slot[k] >= 0)
-                v[k] = ld_stream16(reinterpret_cast<const uint8_t*>(p.kv_c + (t0 + k) * p.kv_c_stride) + 16 * lane);
-        // RoPE (128 B bf16 per token): lanes 0..31, 8 lanes x 16 B per token.
-        const int rk = (lane >> 3) & 3, rc = lane & 7;
-        const int64_t rslot = rk == 0 ? slot[0] : rk == 1 ? slot[1] : rk == 2 ? slot[2] : slot[3];
-        uint4 r = make_uint4(0, 0, 0, 0);
-        if (lane < 32 && rslot >= 0)
-            r = ld_stream16(reinterpret_cast<const uint8_t*>(p.k_pe + (t0 + rk) * p.k_pe_stride) + 16 * rc);
+    for (int k = 0; k < kF8TokPerWave; k++)
+        if (slot[k] >= 0)
+            v[k] = ld_stream16(reinterpret_cast<const uint8_t*>(p.kv_c + (t0 + k) * p.kv_c_stride) + 16 * lane);
+    // RoPE (128 B bf16 per token): 8 lanes x 16 B per token, copied as is.
+    const int rk = (lane >> 3) & (kF8TokPerWave - 1), rc = lane & 7;
+    const int64_t rslot = rk == 0 ? slot[0] : slot[1];
+    const bool rope_lane = lane < 8 * kF8TokPerWave && rslot >= 0;
+    uint4 r = make_uint4(0, 0, 0, 0);
+    if (rope_lane)
+        r = ld_stream16(reinterpret_cast<const uint8_t*>(p.k_pe + (t0 + rk) * p.k_pe_stride) + 16 * rc);
 
 #pragma unroll
-        for (int k = 0; k < kF8TokPerWave; k++) {
-            if (slot[k] < 0) continue;                   // wave-uniform: DPP below sees all lanes
-            const uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
-            float x[8];
+    for (int k = 0; k < kF8TokPerWave; k++) {
+        if (slot[k] < 0) continue;                       // wave-uniform: DPP below sees all lanes
+        const uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+        float x[8];
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
-                x[2 * i] = bf16_lo(w[i]);
-                x[2 * i + 1] = bf16_hi(w[i]);
-            }
-            float amax = 0.0f;
-#pragma unroll
-            for (int i = 0; i < 8; i++) amax = fmaxf(amax, fabsf(x[i]));
-            // 16 lanes x 8 values = one 128-value group: butterfly max in the row.
-            amax = fmaxf(amax, dpp_f32<0xB1>(amax));    // quad_perm [1,0,3,2]
-            amax = fmaxf(amax, dpp_f32<0x4E>(amax));    // quad_perm [2,3,0,1]
-            amax = fmaxf(amax, dpp_f32<0x141>(amax));   // row_half_mirror
-            amax = fmaxf(amax, dpp_f32<0x140>(amax));   // row_mirror
-
-            const float sc = amax / 448.0f;
-            const float inv = (sc == 0.0f) ? 0.0f : 1.0f / sc;
-            uint32_t q0 = 0, q1 = 0;
-            q0 = put_e4m3x2<false>(q0, x[0] * inv, x[1] * inv);
-            q0 = put_e4m3x2<true>(q0, x[2] * inv, x[3] * inv);
-            q1 = put_e4m3x2<false>(q1, x[4] * inv, x[5] * inv);
-            q1 = put_e4m3x2<true>(q1, x[6] * inv, x[7] * inv);
-
-            int64_t blk, off;
-            split_block(slot[k], p.div, blk, off);
-            uint8_t* e = p.cache + blk * p.block_stride + off * p.entry_stride;
-            st_stream8(e + 8 * lane, make_uint2(q0, q1));
-            if ((lane & 15) == 0) st_stream4(e + kF8ScaleOff + 4 * (lane >> 4), __float_as_uint(sc));
+        for (int i = 0; i < 4; i++) {
+            x[2 * i] = bf16_lo(w[i]);
+            x[2 * i + 1] = bf16_hi(w[i]);
         }
-        if (lane < 32 && rslot >= 0) {
-            int64_t blk, off;
-            split_block(rslot, p.div, blk, off);
-            st_stream16(p.cache + blk * p.block_stride + off * p.entry_stride + kF8RopeOff + 16 * rc, r);
-        }
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; i++) amax = fmaxf(amax, fabsf(x[i]));
+        // 16 lanes x 8 values = one 128-value group: butterfly max in the row.
+        amax = fmaxf(amax, dpp_f32<0xB1>(amax));    // quad_perm [1,0,3,2]
+        amax = fmaxf(amax, dpp_f32<0x4E>(amax));    // quad_perm [2,3,0,1]
+        amax = fmaxf(amax, dpp_f32<0x141>(amax));   // row_half_mirror
+        amax = fmaxf(amax, dpp_f32<0x140>(amax));   // row_mirror
+
+        const float sc = amax / 448.0f;
+        const float inv = (sc == 0.0f) ? 0.0f : 1.0f / sc;
+        uint32_t q0 = 0, q1 = 0;
+        q0 = put_e4m3x2<false>(q0, x[0] * inv, x[1] * inv);
+        q0 = put_e4m3x2<true>(q0, x[2] * inv, x[3] * inv);
+        q1 = put_e4m3x2<false>(q1, x[4] * inv, x[5] * inv);
+        q1 = put_e4m3x2<true>(q1, x[6] * inv, x[7] * inv);
+
+        int64_t blk, off;
+        split_block(slot[k], p.div, blk, off);
+        uint8_t* e = p.cache + blk * p.block_stride + off * p.entry_stride;
+        st_stream8(e + 8 * lane, make_uint2(q0, q1));
+        if ((lane & 15) == 0) st_stream4(e + kF8ScaleOff + 4 * (lane >> 4), __float_as_uint(sc));
+    }
+    if (rope_lane) {
+        int64_t blk, off;
+        split_block(rslot, p.div, blk, off);
+        st_stream16(p.cache + blk * p.block_stride + off * p.entry_stride + kF8RopeOff + 16 * rc, r);
     }
 }
 
 // ---------------------------------------------------------------------------
 // gathers
 // ---------------------------------------------------------------------------
-constexpr int kRowsPerWave = 8;
-constexpr int kWalkLds = 1024;     // workspace_starts / seq_starts staged in LDS up to this batch
+constexpr int kRowsPerWave = 4;
 
-// Cache byte offset of the entry read by workspace row r; the request search
-// runs over the LDS copy when the batch fits, else over global memory.
-__device__ __forceinline__ int64_t row_entry_offset(const DsMlaGatherParams& p, const int32_t* s_ws,
-                                                    const int32_t* s_ss, bool lds, int64_t r) {
-    int b;
-    int64_t wsb, ssb;
-    if (lds) {
-        b = find_request(s_ws, p.batch, r);
-        wsb = s_ws[b];
-        ssb = s_ss[b];
-    } else {
-        b = find_request(p.ws, p.batch, r);
-        wsb = p.ws[b];
-        ssb = p.seq_starts ? p.seq_starts[b] : 0;
-    }
-    const int64_t pos = ssb + (r - wsb);
+// Cache byte offset of the entry read by workspace row r.
+__device__ __forceinline__ int64_t row_entry_offset(const DsMlaGatherParams& p, int64_t r) {
+    const int b = find_request(p.ws, p.batch, r, p.total);
+    const int64_t pos = (p.seq_starts ? (int64_t)p.seq_starts[b] : 0) + (r - (int64_t)p.ws[b]);
     int64_t bi, off;
     split_block(pos, p.div, bi, off);
     const int64_t blk = p.block_table[(int64_t)b * p.bt_stride + bi];
@@ -211,26 +200,16 @@ __device__ __forceinline__ int64_t shfl64(int64_t v, int src_lane) {
 }
 
 template <bool NVFP4>
-__global__ __launch_bounds__(kBlockThreads) void k_gather_ds_mla(DsMlaGatherParams p) {
-    __shared__ int32_t s_ws[kWalkLds], s_ss[kWalkLds];
-    const bool lds = p.batch <= kWalkLds;
-    if (lds) {
-        for (int i = threadIdx.x; i < p.batch; i += kBlockThreads) {
-            s_ws[i] = p.ws[i];
-            s_ss[i] = p.seq_starts ? p.seq_starts[i] : 0;
-        }
-        __syncthreads();
-    }
+__global__ __launch_bounds__(kBlockThreads) void k_gather_ds_mla(DsMlaGatherParams p, int64_t wave0) {
     const int lane = lane_id();
-    const int64_t ngroups = (p.total + kRowsPerWave - 1) / kRowsPerWave;
-    const int64_t step = (int64_t)gridDim.x * kWavesPerBlock;
-    for (int64_t g = (int64_t)blockIdx.x * kWavesPerBlock + wave_id(); g < ngroups; g += step) {
-        const int64_t r0 = g * kRowsPerWave;
+    const int64_t r0 = (wave0 + (int64_t)blockIdx.x * kWavesPerBlock + wave_id()) * kRowsPerWave;
+    if (r0 >= p.total) return;
+    {
         const int nrows = (int)min((int64_t)kRowsPerWave, p.total - r0);
         int64_t eoff = 0;
-        if (lane < nrows) eoff = row_entry_offset(p, s_ws, s_ss, lds, r0 + lane);
+        if (lane < nrows) eoff = row_entry_offset(p, r0 + lane);
 
-        // Issue every load of the 8 rows first, then convert and store.
+        // Issue every load of the rows first, then convert and store.
         uint32_t a32[kRowsPerWave];      // nvfp4: 8 codes; fp8: scale bits
         uint2 a64[kRowsPerWave];         // fp8: 8 codes
 #pragma unroll
@@ -245,7 +224,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_gather_ds_mla(DsMlaGatherPara
                 a32[k] = ld_stream4(e + kF8ScaleOff + 4 * (lane >> 4));        // group scale
             }
         }
-        // RoPE: lane -> row lane/8, 8 values (16 B out) per lane.
+        // RoPE: lane -> row lane/8 (lanes 0..8*rows-1), 8 values (16 B out) per lane.
         const int rk = lane >> 3, rc = lane & 7;
         const int64_t reo = shfl64(eoff, rk);
         uint4 rv = make_uint4(0, 0, 0, 0);
@@ -297,18 +276,16 @@ __global__ __launch_bounds__(kBlockThreads) void k_gather_ds_mla(DsMlaGatherPara
 // launchers
 // ---------------------------------------------------------------------------
 hipError_t launch_write_nvfp4_ds_mla(const DsMlaWriteParams& p, hipStream_t s) {
-    return launch1(k_write_nvfp4_ds_mla, grid_for_waves((p.num_tokens + kNvTokPerWave - 1) / kNvTokPerWave), s, p);
+    return launch_waves(k_write_nvfp4_ds_mla, (p.num_tokens + kNvTokPerWave - 1) / kNvTokPerWave, s, p);
 }
 hipError_t launch_write_fp8_ds_mla(const DsMlaWriteParams& p, hipStream_t s) {
-    return launch1(k_write_fp8_ds_mla, grid_for_waves((p.num_tokens + kF8TokPerWave - 1) / kF8TokPerWave), s, p);
+    return launch_waves(k_write_fp8_ds_mla, (p.num_tokens + kF8TokPerWave - 1) / kF8TokPerWave, s, p);
 }
 hipError_t launch_gather_nvfp4_ds_mla(const DsMlaGatherParams& p, hipStream_t s) {
-    return launch1(k_gather_ds_mla<true>,
-                   grid_for_waves((p.total + kRowsPerWave - 1) / kRowsPerWave), s, p);
+    return launch_waves(k_gather_ds_mla<true>, (p.total + kRowsPerWave - 1) / kRowsPerWave, s, p);
 }
 hipError_t launch_gather_fp8_ds_mla(const DsMlaGatherParams& p, hipStream_t s) {
-    return launch1(k_gather_ds_mla<false>,
-                   grid_for_waves((p.total + kRowsPerWave - 1) / kRowsPerWave), s, p);
+    return launch_waves(k_gather_ds_mla<false>, (p.total + kRowsPerWave - 1) / kRowsPerWave, s, p);
 }
 
 }  // namespace gcache

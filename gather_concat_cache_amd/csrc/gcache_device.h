@@ -146,11 +146,36 @@ __device__ __forceinline__ void split_block(int64_t pos, const BlockDiv& d, int6
 }
 
 // Gather walk: request of workspace row r = the largest b < batch with
-// ws[b] <= r (binary search; ws non-decreasing, ws[0] == 0).
-__device__ __forceinline__ int find_request(const int32_t* __restrict__ ws, int batch, int64_t r) {
-    int lo = 0, hi = batch;                        // ws[lo] <= r, answer in [lo, hi)
+// ws[b] <= r (ws non-decreasing, ws[0] == 0).  The search starts at the
+// interpolated guess r * batch / total and gallops outwards, then bisects the
+// bracket: about two probes when requests are evenly sized (one row per
+// request, for instance) and at most about twice a plain bisection.
+__host__ __device__ __forceinline__ int find_request(const int32_t* __restrict__ ws, int batch, int64_t r,
+                                           int64_t total) {
+    int lo, hi;                                    // invariant: ws[lo] <= r < ws[hi] (hi == batch: +inf)
+    int g = (int)((r * (int64_t)batch) / total);
+    if (g >= batch) g = batch - 1;
+    if ((int64_t)ws[g] <= r) {
+        lo = g;
+        int step = 1;
+        hi = g + 1;
+        while (hi < batch && (int64_t)ws[hi] <= r) {
+            lo = hi;
+            step <<= 1;
+            hi = (lo + step < batch) ? lo + step : batch;
+        }
+    } else {
+        hi = g;
+        int step = 1;
+        lo = g - 1;                                // g >= 1 here since ws[0] == 0 <= r
+        while ((int64_t)ws[lo] > r) {
+            hi = lo;
+            step <<= 1;
+            lo = (hi - step > 0) ? hi - step : 0;
+        }
+    }
     while (hi - lo > 1) {
-        int mid = (lo + hi) >> 1;
+        const int mid = (lo + hi) >> 1;
         if ((int64_t)ws[mid] <= r) lo = mid; else hi = mid;
     }
     return lo;

@@ -77,20 +77,23 @@ hipError_t launch_gather_fp8_ds_mla(const DsMlaGatherParams& p, hipStream_t s);
 hipError_t launch_reshape_and_cache_nvfp4(const KvWriteParams& p, hipStream_t s);
 hipError_t launch_gather_nvfp4_kv(const KvGatherParams& p, hipStream_t s);
 
-// Workgroups for `waves` independent wave-sized work items (grid-stride
-// loops cover anything beyond the cap).
-inline unsigned grid_for_waves(int64_t waves) {
-    int64_t blocks = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
-    const int64_t cap = int64_t(1) << 22;
-    if (blocks < 1) blocks = 1;
-    return (unsigned)(blocks < cap ? blocks : cap);
-}
-
+// Launch `waves` one-shot waves of `kernel(params, wave0)`: the kernel's
+// wave index is wave0 + blockIdx.x * kWavesPerBlock + wave_id().  Grids are
+// split into launches of at most 2^24 workgroups (far beyond any realistic
+// shape); each piece passes its first wave index.
 template <typename P>
-inline hipError_t launch1(void (*kernel)(P), unsigned blocks, hipStream_t s, const P& p) {
-    void* args[] = {const_cast<P*>(&p)};
-    return hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3(blocks), dim3(kBlockThreads),
-                           args, 0, s);
+inline hipError_t launch_waves(void (*kernel)(P, int64_t), int64_t waves, hipStream_t s, const P& p) {
+    const int64_t kMaxBlocks = int64_t(1) << 24;
+    const int64_t blocks = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
+    for (int64_t b0 = 0; b0 < blocks; b0 += kMaxBlocks) {
+        const int64_t nb = blocks - b0 < kMaxBlocks ? blocks - b0 : kMaxBlocks;
+        int64_t wave0 = b0 * kWavesPerBlock;
+        void* args[] = {const_cast<P*>(&p), &wave0};
+        const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3((unsigned)nb),
+                                             dim3(kBlockThreads), args, 0, s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace gcache

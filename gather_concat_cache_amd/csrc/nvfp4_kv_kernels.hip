@@ -5,12 +5,12 @@
 // rows and NHD/HND orders all use the same kernels.
 //
 // Mapping (HBM-bound, no contraction; streaming loads and stores):
-//   write  : one wave per token; one lane per 16-value block of a head and
+//   write  : one-shot wave per token; one lane per 16-value block of a head and
 //            side (32 B in, 8 B data + 1 scale byte out).  With 8 heads of
 //            128 values a side is exactly 64 blocks, so both sides' loads
 //            (64 B per lane) are in flight before any is used.
-//   gather : four workspace rows per wave; lanes 0..3 resolve the rows'
-//            cache addresses (binary search over workspace_starts, one
+//   gather : four workspace rows per one-shot wave; lanes 0..3 resolve the
+//            rows' cache addresses (search over workspace_starts, one
 //            block-table load), then every (row, side) is read and written
 //            by the whole wave, one lane per 8 values (4 data bytes in,
 //            16 B bf16 out).
@@ -30,15 +30,16 @@ __device__ __forceinline__ void split_pow2(int v, int shift, int n, int& q, int&
 
 constexpr int kKvItemsPerLane = 2;   // blocks in flight per lane and pass
 
-__global__ __launch_bounds__(kBlockThreads) void k_reshape_and_cache_nvfp4(KvWriteParams p) {
+__global__ __launch_bounds__(kBlockThreads) void k_reshape_and_cache_nvfp4(KvWriteParams p, int64_t wave0) {
     const int lane = lane_id();
     const int bph = p.head_size >> 4;                    // 16-value blocks per head
     const int nblk = p.num_heads * bph;                  // per side
     const int nitems = 2 * nblk;                         // both sides
-    const int64_t step = (int64_t)gridDim.x * kWavesPerBlock;
-    for (int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + wave_id(); t < p.num_tokens; t += step) {
+    const int64_t t = wave0 + (int64_t)blockIdx.x * kWavesPerBlock + wave_id();
+    if (t >= p.num_tokens) return;
+    {
         const int64_t slot = p.slots[t];
-        if (slot < 0) continue;                           // padding token (wave-uniform)
+        if (slot < 0) return;                             // padding token (wave-uniform)
         int64_t blk, off;
         split_block(slot, p.div, blk, off);
         const float gs_k = *p.gscale[0], gs_v = *p.gscale[1];
@@ -104,22 +105,21 @@ __global__ __launch_bounds__(kBlockThreads) void k_reshape_and_cache_nvfp4(KvWri
 
 constexpr int kKvRowsPerWave = 4;
 
-__global__ __launch_bounds__(kBlockThreads) void k_gather_nvfp4_kv(KvGatherParams p) {
+__global__ __launch_bounds__(kBlockThreads) void k_gather_nvfp4_kv(KvGatherParams p, int64_t wave0) {
     const int lane = lane_id();
     const int cph = p.head_size >> 3;                    // 8-value chunks per head
     const int nchunk = p.num_heads * cph;                // per side
-    const int64_t ngroups = (p.total + kKvRowsPerWave - 1) / kKvRowsPerWave;
-    const int64_t step = (int64_t)gridDim.x * kWavesPerBlock;
+    const int64_t r0 = (wave0 + (int64_t)blockIdx.x * kWavesPerBlock + wave_id()) * kKvRowsPerWave;
+    if (r0 >= p.total) return;
     const float gs_k = *p.gscale[0], gs_v = *p.gscale[1];
-    for (int64_t g = (int64_t)blockIdx.x * kWavesPerBlock + wave_id(); g < ngroups; g += step) {
-        const int64_t r0 = g * kKvRowsPerWave;
+    {
         const int nrows = (int)min((int64_t)kKvRowsPerWave, p.total - r0);
         // lanes 0..nrows-1: (block, offset) of their row (block ids are int32
         // table entries, offsets < block_size, so 32 bits carry both)
         int32_t my_blk = 0, my_off = 0;
         if (lane < nrows) {
             const int64_t r = r0 + lane;
-            const int b = find_request(p.ws, p.batch, r);
+            const int b = find_request(p.ws, p.batch, r, p.total);
             const int64_t pos = (p.seq_starts ? (int64_t)p.seq_starts[b] : 0) + (r - (int64_t)p.ws[b]);
             int64_t bi, o;
             split_block(pos, p.div, bi, o);
@@ -171,10 +171,10 @@ __global__ __launch_bounds__(kBlockThreads) void k_gather_nvfp4_kv(KvGatherParam
 }
 
 hipError_t launch_reshape_and_cache_nvfp4(const KvWriteParams& p, hipStream_t s) {
-    return launch1(k_reshape_and_cache_nvfp4, grid_for_waves(p.num_tokens), s, p);
+    return launch_waves(k_reshape_and_cache_nvfp4, p.num_tokens, s, p);
 }
 hipError_t launch_gather_nvfp4_kv(const KvGatherParams& p, hipStream_t s) {
-    return launch1(k_gather_nvfp4_kv, grid_for_waves((p.total + kKvRowsPerWave - 1) / kKvRowsPerWave), s, p);
+    return launch_waves(k_gather_nvfp4_kv, (p.total + kKvRowsPerWave - 1) / kKvRowsPerWave, s, p);
 }
 
 }  // namespace gcache
