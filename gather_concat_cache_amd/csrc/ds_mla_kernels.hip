@@ -209,7 +209,10 @@ __global__ __launch_bounds__(kBlockThreads) void k_gather_ds_mla(DsMlaGatherPara
         int64_t eoff = 0;
         if (lane < nrows) eoff = row_entry_offset(p, r0 + lane);
 
-        // Issue every load of the rows first, then convert and store.
+        // Issue every load of the rows first, then convert and store.  The
+        // nvfp4 scale of lane l's values (block l/2, byte 320 + l/2) is read
+        // with its dword and shifted down.
+        const int sf_shift = 8 * ((lane >> 1) & 3);
         uint32_t a32[kRowsPerWave];      // nvfp4: 8 codes; fp8: scale bits
         uint2 a64[kRowsPerWave];         // fp8: 8 codes
 #pragma unroll
@@ -218,7 +221,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_gather_ds_mla(DsMlaGatherPara
             const uint8_t* e = p.cache + readlane64(eoff, k);
             if (NVFP4) {
                 a32[k] = ld_stream4(e + 4 * lane);                             // values 8l..8l+7
-                a64[k].x = ld_stream1(e + kNvScaleOff + (lane >> 1));          // their scale
+                a64[k].x = ld_stream4(e + kNvScaleOff + 4 * (lane >> 3));      // scales 4(l/8)..+3
             } else {
                 a64[k] = ld_stream8(e + 8 * lane);                             // codes 8l..8l+7
                 a32[k] = ld_stream4(e + kF8ScaleOff + 4 * (lane >> 4));        // group scale
@@ -245,7 +248,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_gather_ds_mla(DsMlaGatherPara
             uint4 o;
             if (NVFP4) {
                 const uint32_t nib = a32[k];
-                const float s = e4m3_f32(a64[k].x);
+                const float s = e4m3_f32(a64[k].x >> sf_shift);              // scale of block l/2
                 const f32x2 a = e2m1x2_f32<0>(nib), b = e2m1x2_f32<1>(nib);
                 const f32x2 c = e2m1x2_f32<2>(nib), d = e2m1x2_f32<3>(nib);
                 o = make_uint4(pack_bf16x2(a.x * s, a.y * s), pack_bf16x2(b.x * s, b.y * s),

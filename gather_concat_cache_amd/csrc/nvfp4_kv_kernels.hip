@@ -9,11 +9,11 @@
 //            side (32 B in, 8 B data + 1 scale byte out).  With 8 heads of
 //            128 values a side is exactly 64 blocks, so both sides' loads
 //            (64 B per lane) are in flight before any is used.
-//   gather : four workspace rows per one-shot wave; lanes 0..3 resolve the
-//            rows' cache addresses (search over workspace_starts, one
-//            block-table load), then every (row, side) is read and written
-//            by the whole wave, one lane per 8 values (4 data bytes in,
-//            16 B bf16 out).
+//   gather : one workspace row per one-shot wave (both sides, all heads);
+//            the row's cache address is resolved once (wave-uniform search
+//            over workspace_starts, one block-table load), then one lane per
+//            8 values (4 data bytes in, 16 B bf16 out), every load of a pass
+//            issued before any conversion.
 #include "gcache_internal.h"
 
 namespace gcache {
@@ -103,69 +103,56 @@ __global__ __launch_bounds__(kBlockThreads) void k_reshape_and_cache_nvfp4(KvWri
     }
 }
 
-constexpr int kKvRowsPerWave = 4;
+constexpr int kKvGatherItems = 4;   // 8-value chunks per lane and pass
 
 __global__ __launch_bounds__(kBlockThreads) void k_gather_nvfp4_kv(KvGatherParams p, int64_t wave0) {
     const int lane = lane_id();
     const int cph = p.head_size >> 3;                    // 8-value chunks per head
     const int nchunk = p.num_heads * cph;                // per side
-    const int64_t r0 = (wave0 + (int64_t)blockIdx.x * kWavesPerBlock + wave_id()) * kKvRowsPerWave;
-    if (r0 >= p.total) return;
+    const int nitems = 2 * nchunk;                       // both sides
+    const int64_t r = wave0 + (int64_t)blockIdx.x * kWavesPerBlock + wave_id();
+    if (r >= p.total) return;
+    // wave-uniform walk of row r
+    const int b = find_request(p.ws, p.batch, r, p.total);
+    const int64_t pos = (p.seq_starts ? (int64_t)p.seq_starts[b] : 0) + (r - (int64_t)p.ws[b]);
+    int64_t bi, off;
+    split_block(pos, p.div, bi, off);
+    const int64_t blk = p.block_table[(int64_t)b * p.bt_stride + bi];
     const float gs_k = *p.gscale[0], gs_v = *p.gscale[1];
-    {
-        const int nrows = (int)min((int64_t)kKvRowsPerWave, p.total - r0);
-        // lanes 0..nrows-1: (block, offset) of their row (block ids are int32
-        // table entries, offsets < block_size, so 32 bits carry both)
-        int32_t my_blk = 0, my_off = 0;
-        if (lane < nrows) {
-            const int64_t r = r0 + lane;
-            const int b = find_request(p.ws, p.batch, r, p.total);
-            const int64_t pos = (p.seq_starts ? (int64_t)p.seq_starts[b] : 0) + (r - (int64_t)p.ws[b]);
-            int64_t bi, o;
-            split_block(pos, p.div, bi, o);
-            my_off = (int32_t)o;
-            my_blk = p.block_table[(int64_t)b * p.bt_stride + bi];
-        }
-        for (int k = 0; k < nrows; k++) {
-            const int64_t blk = __builtin_amdgcn_readlane(my_blk, k);
-            const int64_t off = __builtin_amdgcn_readlane(my_off, k);
-            const int64_t r = r0 + k;
-            // both sides' chunks of this row: 2 * nchunk items, loads first
-            for (int base = 0; base < 2 * nchunk; base += 2 * kWave) {
-                uint32_t nib[2], sfb[2];
+
+    for (int base = 0; base < nitems; base += kKvGatherItems * kWave) {
+        uint32_t nib[kKvGatherItems], sfb[kKvGatherItems];
 #pragma unroll
-                for (int u = 0; u < 2; u++) {
-                    const int it = base + u * kWave + lane;
-                    if (it < 2 * nchunk) {
-                        const int side = it >= nchunk;
-                        int h, i;
-                        split_pow2(it - side * nchunk, p.cph_shift, cph, h, i);  // values 8i..8i+7 of head h
-                        const uint8_t* sb = p.cache + blk * p.L.block_stride + side * p.L.side_stride;
-                        nib[u] = ld_stream4(sb + p.L.data_offset + off * p.L.data_token_stride
-                                            + h * p.L.data_head_stride + 4 * i);
-                        sfb[u] = ld_stream1(sb + p.L.scale_offset + off * p.L.scale_token_stride
-                                            + h * p.L.scale_head_stride + (i >> 1));
-                    }
-                }
-#pragma unroll
-                for (int u = 0; u < 2; u++) {
-                    const int it = base + u * kWave + lane;
-                    if (it >= 2 * nchunk) continue;
-                    const int side = it >= nchunk;
-                    int h, i;
-                    split_pow2(it - side * nchunk, p.cph_shift, cph, h, i);
-                    const float gs = side ? gs_v : gs_k;
-                    const float s = e4m3_f32(sfb[u]);
-                    const f32x2 a = e2m1x2_f32<0>(nib[u]), bb = e2m1x2_f32<1>(nib[u]);
-                    const f32x2 cc = e2m1x2_f32<2>(nib[u]), d = e2m1x2_f32<3>(nib[u]);
-                    // (e2m1 * e4m3) is exact; one rounding for * gs, one for bf16.
-                    const uint4 o = make_uint4(pack_bf16x2((a.x * s) * gs, (a.y * s) * gs),
-                                               pack_bf16x2((bb.x * s) * gs, (bb.y * s) * gs),
-                                               pack_bf16x2((cc.x * s) * gs, (cc.y * s) * gs),
-                                               pack_bf16x2((d.x * s) * gs, (d.y * s) * gs));
-                    st_stream16(p.out[side] + r * p.token_stride[side] + h * p.head_stride[side] + 8 * i, o);
-                }
+        for (int u = 0; u < kKvGatherItems; u++) {       // all loads of the pass first
+            const int it = base + u * kWave + lane;
+            if (it < nitems) {
+                const int side = it >= nchunk;
+                int h, i;
+                split_pow2(it - side * nchunk, p.cph_shift, cph, h, i);   // values 8i..8i+7 of head h
+                const uint8_t* sb = p.cache + blk * p.L.block_stride + side * p.L.side_stride;
+                nib[u] = ld_stream4(sb + p.L.data_offset + off * p.L.data_token_stride
+                                    + h * p.L.data_head_stride + 4 * i);
+                sfb[u] = ld_stream1(sb + p.L.scale_offset + off * p.L.scale_token_stride
+                                    + h * p.L.scale_head_stride + (i >> 1));
             }
+        }
+#pragma unroll
+        for (int u = 0; u < kKvGatherItems; u++) {
+            const int it = base + u * kWave + lane;
+            if (it >= nitems) continue;
+            const int side = it >= nchunk;
+            int h, i;
+            split_pow2(it - side * nchunk, p.cph_shift, cph, h, i);
+            const float gs = side ? gs_v : gs_k;
+            const float s = e4m3_f32(sfb[u]);
+            const f32x2 a = e2m1x2_f32<0>(nib[u]), bb = e2m1x2_f32<1>(nib[u]);
+            const f32x2 cc = e2m1x2_f32<2>(nib[u]), d = e2m1x2_f32<3>(nib[u]);
+            // (e2m1 * e4m3) is exact; one rounding for * gs, one for bf16.
+            const uint4 o = make_uint4(pack_bf16x2((a.x * s) * gs, (a.y * s) * gs),
+                                       pack_bf16x2((bb.x * s) * gs, (bb.y * s) * gs),
+                                       pack_bf16x2((cc.x * s) * gs, (cc.y * s) * gs),
+                                       pack_bf16x2((d.x * s) * gs, (d.y * s) * gs));
+            st_stream16(p.out[side] + r * p.token_stride[side] + h * p.head_stride[side] + 8 * i, o);
         }
     }
 }
@@ -174,7 +161,7 @@ hipError_t launch_reshape_and_cache_nvfp4(const KvWriteParams& p, hipStream_t s)
     return launch_waves(k_reshape_and_cache_nvfp4, p.num_tokens, s, p);
 }
 hipError_t launch_gather_nvfp4_kv(const KvGatherParams& p, hipStream_t s) {
-    return launch_waves(k_gather_nvfp4_kv, (p.total + kKvRowsPerWave - 1) / kKvRowsPerWave, s, p);
+    return launch_waves(k_gather_nvfp4_kv, p.total, s, p);
 }
 
 }  // namespace gcache
