@@ -46,6 +46,10 @@ def parse():
     ap.add_argument("--cold", action="store_true",
                     help="also time every kernel once per run after evicting the caches")
     ap.add_argument("--only", default=None, help="comma list of op names to run (profiling aid)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="also run a plain elementwise kernel reading and writing MIB MiB, three "
+                         "times, outside the timed region, so HBM counters can be scaled against "
+                         "known bytes")
     return ap.parse_args()
 
 
@@ -174,6 +178,18 @@ def main():
         kernels[name] = {"ms": round(ms, 5), "bytes": nbytes, "units": units,
                          "GB_per_s": round(nbytes / (ms * 1e6), 1),
                          "frac_of_hbm_peak": round(nbytes / (ms * 1e6) / HBM_PEAK_GBS, 4)}
+
+    if args.copy_calibration:
+        # a plain elementwise kernel that reads and writes exactly n bytes each
+        # (torch's copy_ of two device buffers goes to a DMA engine instead)
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+        torch.cuda.synchronize()
+        for _ in range(3):
+            torch.add(src, 1, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     cold = None
     if args.cold:

@@ -230,7 +230,8 @@ def test_perhead_layouts(g, orc, variant):
     seed = {"interleaved": 41, "hnd": 42, "odd-head-size": 43, "strided-input": 44}[variant]
     rng = np.random.default_rng(seed)
     # head size 80: 5 scale blocks and 10 chunks per head (the non-power-of-two paths)
-    H, hs, nb, bs = (3, 80, 20, 16) if variant == "odd-head-size" else (4, 64, 16, 16)
+    # interleaved [data | scales] rows keep 8-byte data alignment at head size 128 (72-byte rows)
+    H, hs, nb, bs = {"odd-head-size": (3, 80, 20, 16), "interleaved": (4, 128, 16, 16)}.get(variant, (4, 64, 16, 16))
     T = 157
     key, value, slots = _kv_case(rng, T, H, hs, nb, bs, 9)
     ks, vs = synth.global_scale(key), synth.global_scale(value)
