@@ -50,6 +50,9 @@ def parse():
                     help="also run a plain elementwise kernel reading and writing MIB MiB, three "
                          "times, outside the timed region, so HBM counters can be scaled against "
                          "known bytes")
+    ap.add_argument("--traffic-from", nargs=2, default=None, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="host only: turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then "
+                         "WRITE_SIZE, each with --copy-calibration) into profiles/traffic.json")
     return ap.parse_args()
 
 
@@ -88,6 +91,9 @@ def kv_gather_bytes(g, H, hs):
 # ---------------------------------------------------------------------------
 def main():
     args = parse()
+    if args.traffic_from:
+        write_traffic(*args.traffic_from)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
               "(the path is token-parallel; see the design notes for how it shards).", file=sys.stderr)
@@ -261,6 +267,68 @@ def traffic_for(kernel):
         return t["kernels"].get(kernel, {}).get("hbm_bytes_per_launch")
     except Exception:
         return None
+
+
+# kernel symbol (prefix up to the parameter list) -> op name used above
+KERNEL_OPS = {
+    "gcache::k_write_nvfp4_ds_mla": "nvfp4_ds_mla_write",
+    "gcache::k_write_fp8_ds_mla": "fp8_ds_mla_write",
+    "void gcache::k_gather_ds_mla<true>": "nvfp4_ds_mla_gather",
+    "gcache::k_reshape_and_cache_nvfp4": "nvfp4_kv_write",
+    "void gcache::k_gather_ds_mla<false>": "fp8_ds_mla_gather",
+    "gcache::k_gather_nvfp4_kv": "nvfp4_kv_gather",
+}
+CALIBRATION_KERNEL = "CUDAFunctorOnSelf_add"
+
+
+def write_traffic(fetch_dir, write_dir):
+    """Scale the per-dispatch FETCH_SIZE and WRITE_SIZE counters (KiB) of each
+    kernel by what the same counter reads for the calibration kernel, an
+    elementwise add that reads and writes exactly --copy-calibration MiB each,
+    and store the mean HBM bytes per launch with the current library digest."""
+    import csv
+    import glob
+    from gather_concat_cache_amd.build import source_digest
+
+    def per_kernel(d, counter):
+        (path,) = glob.glob(os.path.join(d, "*counter_collection.csv"))
+        vals = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            name = r["Kernel_Name"]
+            key = next((op for k, op in KERNEL_OPS.items() if name.startswith(k + "(")), None)
+            if key is None and CALIBRATION_KERNEL in name:
+                key = "calibration"
+            if key is not None:
+                vals.setdefault(key, []).append(float(r["Counter_Value"]))
+        return vals
+
+    fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
+    cal_mib = 1024
+    cal_kib = cal_mib * 1024.0
+    f_scale = cal_kib / float(np.mean(fetch["calibration"]))
+    w_scale = cal_kib / float(np.mean(write["calibration"]))
+    w3, g3, w4, g4, w5, g5 = build_workloads()
+    H, hs = w5.key.shape[1], w5.key.shape[2]
+    algo = {"nvfp4_ds_mla_write": ds_write_bytes(w3, NV), "fp8_ds_mla_write": ds_write_bytes(w4, F8),
+            "nvfp4_ds_mla_gather": ds_gather_bytes(g3, NV), "nvfp4_kv_write": kv_write_bytes(w5),
+            "fp8_ds_mla_gather": ds_gather_bytes(g4, F8), "nvfp4_kv_gather": kv_gather_bytes(g5, H, hs)}
+    out = {"source_digest": source_digest(), "calibration_mib": cal_mib,
+           "fetch_scale": round(f_scale, 5), "write_scale": round(w_scale, 5), "kernels": {}}
+    for op in KERNEL_OPS.values():
+        fb = float(np.mean(fetch[op])) * 1024 * f_scale
+        wb = float(np.mean(write[op])) * 1024 * w_scale
+        out["kernels"][op] = {"dispatches": [len(fetch[op]), len(write[op])],
+                              "fetch_kib_raw": round(float(np.mean(fetch[op])), 1),
+                              "write_kib_raw": round(float(np.mean(write[op])), 1),
+                              "hbm_bytes_per_launch": int(round(fb + wb)),
+                              "algorithmic_bytes": algo[op],
+                              "traffic_over_algorithmic": round((fb + wb) / algo[op], 4)}
+    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out, indent=1))
 
 
 # ---------------------------------------------------------------------------
