@@ -22,10 +22,12 @@
 //   fp8 write   : 8 values per lane (one 16 B load), one token per 64 lanes,
 //                 two tokens per wave; the 128-value group amax is a 4-step
 //                 DPP butterfly inside each 16-lane row.
-//   gathers     : 4 workspace rows per wave; lanes 0..3 resolve the rows'
-//                 cache addresses (search over workspace_starts, one
-//                 block-table load), then each row is read and written by
-//                 the whole wave with contiguous accesses.
+//   gathers     : one workgroup per 16 workspace rows; wave 0 resolves the
+//                 rows' cache addresses (batch <= 64: workspace_starts held
+//                 one per lane and bisected with cross-lane reads, then one
+//                 block-table load), the entries are staged in LDS with
+//                 16-byte loads, and each row is written by a whole wave
+//                 with contiguous 16-byte stores.
 #include "gcache_internal.h"
 
 namespace gcache {
@@ -85,7 +87,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_write_nvfp4_ds_mla(DsMlaWrite
 #pragma unroll
     for (int k = 0; k < 2; k++) {
         const int64_t t = g * kNvTokPerWave + 2 * k + half;
-        slot[k] = (t < p.num_tokens) ? p.slots[t] : -1;
+        slot[k] = (t < p.num_tokens) ? valid_slot(p.slots[t], p.num_slots) : -1;
     }
 #pragma unroll
     for (int k = 0; k < 2; k++) {                        // padding tokens read nothing
@@ -119,7 +121,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_write_fp8_ds_mla(DsMlaWritePa
     int64_t slot[kF8TokPerWave];                         // wave-uniform
 #pragma unroll
     for (int k = 0; k < kF8TokPerWave; k++)
-        slot[k] = (t0 + k < p.num_tokens) ? p.slots[t0 + k] : -1;
+        slot[k] = (t0 + k < p.num_tokens) ? valid_slot(p.slots[t0 + k], p.num_slots) : -1;
     uint4 v[kF8TokPerWave];
 #pragma unroll
     for (int k = 0; k < kF8TokPerWave; k++)
@@ -176,102 +178,118 @@ __global__ __launch_bounds__(kBlockThreads) void k_write_fp8_ds_mla(DsMlaWritePa
 // ---------------------------------------------------------------------------
 // gathers
 // ---------------------------------------------------------------------------
-constexpr int kRowsPerWave = 4;
+constexpr int kGatherTile = 16;    // workspace rows per workgroup
 
-// Cache byte offset of the entry read by workspace row r.
-__device__ __forceinline__ int64_t row_entry_offset(const DsMlaGatherParams& p, int64_t r) {
-    const int b = find_request(p.ws, p.batch, r, p.total);
-    const int64_t pos = (p.seq_starts ? (int64_t)p.seq_starts[b] : 0) + (r - (int64_t)p.ws[b]);
-    int64_t bi, off;
-    split_block(pos, p.div, bi, off);
-    const int64_t blk = p.block_table[(int64_t)b * p.bt_stride + bi];
-    return blk * p.block_stride + off * p.entry_stride;
+// Wave 0 resolves the cache offsets of rows r0 .. r0+nrows-1 (lane i: row
+// r0+i); -1 marks a row whose walk leaves the block table or the cache.
+__device__ __forceinline__ int64_t tile_row_entry(const DsMlaGatherParams& p, int64_t r0, int nrows,
+                                                  int lane) {
+    const int64_t r = r0 + lane;
+    int b = 0;
+    int64_t ws_b = 0, ss_b = 0;
+    if (p.batch <= kWave) {
+        // one load of workspace_starts / seq_starts per lane, then a
+        // bisection by cross-lane reads: no dependent global loads
+        const bool in = lane < p.batch;
+        const int32_t wsl = in ? p.ws[lane] : 0x7FFFFFFF;
+        const int32_t ssl = (in && p.seq_starts) ? p.seq_starts[lane] : 0;
+        b = bisect_request64([&](int i) { return (int64_t)__shfl(wsl, i); }, p.batch, r);
+        ws_b = __shfl(wsl, b);
+        ss_b = __shfl(ssl, b);
+    } else if (lane < nrows) {
+        b = find_request(p.ws, p.batch, r, p.total);
+        ws_b = p.ws[b];
+        ss_b = p.seq_starts ? p.seq_starts[b] : 0;
+    }
+    if (lane >= nrows) return -1;
+    return row_entry(p.block_table, p.bt_stride, b, ws_b, ss_b, r, p.div, p.num_blocks, p.block_stride,
+                     p.entry_stride);
 }
 
-__device__ __forceinline__ int64_t readlane64(int64_t v, int k) {
-    const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, k);
-    const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)v >> 32), k);
-    return (int64_t)(((uint64_t)hi << 32) | lo);
-}
-__device__ __forceinline__ int64_t shfl64(int64_t v, int src_lane) {
-    const uint32_t lo = __builtin_amdgcn_ds_bpermute(src_lane << 2, (int)(uint32_t)v);
-    const uint32_t hi = __builtin_amdgcn_ds_bpermute(src_lane << 2, (int)(uint32_t)((uint64_t)v >> 32));
-    return (int64_t)(((uint64_t)hi << 32) | lo);
-}
-
+// One workgroup per tile of kGatherTile consecutive workspace rows:
+//   1. wave 0 resolves the rows' entry offsets into LDS;
+//   2. every 16-byte piece of the tile's entries is loaded (all loads in
+//      flight before any is stored) and staged in LDS;
+//   3. each wave converts and stores whole NoPE rows (64 lanes x 16 B), then
+//      the RoPE pieces (8 x 16 B per row) are spread over the workgroup.
+// Rows with an invalid walk are written as zeros.
 template <bool NVFP4>
-__global__ __launch_bounds__(kBlockThreads) void k_gather_ds_mla(DsMlaGatherParams p, int64_t wave0) {
-    const int lane = lane_id();
-    const int64_t r0 = (wave0 + (int64_t)blockIdx.x * kWavesPerBlock + wave_id()) * kRowsPerWave;
-    if (r0 >= p.total) return;
-    {
-        const int nrows = (int)min((int64_t)kRowsPerWave, p.total - r0);
-        int64_t eoff = 0;
-        if (lane < nrows) eoff = row_entry_offset(p, r0 + lane);
+__global__ __launch_bounds__(kBlockThreads) void k_gather_ds_mla(DsMlaGatherParams p, int64_t tile0) {
+    constexpr int EB = NVFP4 ? kNvEntry : kF8Entry;      // entry bytes used
+    constexpr int EC = EB / 16;                          // 16-byte pieces per entry
+    constexpr int kPieces = (kGatherTile * EC + kBlockThreads - 1) / kBlockThreads;
+    __shared__ __align__(16) uint8_t s_ent[kGatherTile * EB];
+    __shared__ int64_t s_off[kGatherTile];
 
-        // Issue every load of the rows first, then convert and store.  The
-        // nvfp4 scale of lane l's values (block l/2, byte 320 + l/2) is read
-        // with its dword and shifted down.
-        const int sf_shift = 8 * ((lane >> 1) & 3);
-        uint32_t a32[kRowsPerWave];      // nvfp4: 8 codes; fp8: scale bits
-        uint2 a64[kRowsPerWave];         // fp8: 8 codes
-#pragma unroll
-        for (int k = 0; k < kRowsPerWave; k++) {
-            if (k >= nrows) continue;
-            const uint8_t* e = p.cache + readlane64(eoff, k);
-            if (NVFP4) {
-                a32[k] = ld_stream4(e + 4 * lane);                             // values 8l..8l+7
-                a64[k].x = ld_stream4(e + kNvScaleOff + 4 * (lane >> 3));      // scales 4(l/8)..+3
-            } else {
-                a64[k] = ld_stream8(e + 8 * lane);                             // codes 8l..8l+7
-                a32[k] = ld_stream4(e + kF8ScaleOff + 4 * (lane >> 4));        // group scale
-            }
-        }
-        // RoPE: lane -> row lane/8 (lanes 0..8*rows-1), 8 values (16 B out) per lane.
-        const int rk = lane >> 3, rc = lane & 7;
-        const int64_t reo = shfl64(eoff, rk);
-        uint4 rv = make_uint4(0, 0, 0, 0);
-        if (rk < nrows) {
-            const uint8_t* e = p.cache + reo;
-            if (NVFP4) {
-                const uint2 q = ld_stream8(e + kNvRopeOff + 8 * rc);
-                rv.x = q.x;
-                rv.y = q.y;
-            } else {
-                rv = ld_stream16(e + kF8RopeOff + 16 * rc);
-            }
-        }
+    const int tid = threadIdx.x;
+    const int64_t r0 = (tile0 + blockIdx.x) * kGatherTile;
+    if (r0 >= p.total) return;                           // workgroup-uniform
+    const int nrows = (int)min((int64_t)kGatherTile, p.total - r0);
+    if (tid < kWave) {
+        const int64_t e = tile_row_entry(p, r0, nrows, tid);
+        if (tid < kGatherTile) s_off[tid] = e;
+    }
+    __syncthreads();
 
+    uint4 v[kPieces];
 #pragma unroll
-        for (int k = 0; k < kRowsPerWave; k++) {
-            if (k >= nrows) continue;
-            uint4 o;
-            if (NVFP4) {
-                const uint32_t nib = a32[k];
-                const float s = e4m3_f32(a64[k].x >> sf_shift);              // scale of block l/2
+    for (int k = 0; k < kPieces; k++) {
+        const int j = tid + kBlockThreads * k;
+        const int row = j / EC;
+        if (j < kGatherTile * EC && row < nrows && s_off[row] >= 0)
+            v[k] = ld_stream16(p.cache + s_off[row] + 16 * (j - row * EC));
+    }
+#pragma unroll
+    for (int k = 0; k < kPieces; k++) {
+        const int j = tid + kBlockThreads * k;
+        const int row = j / EC;
+        if (j < kGatherTile * EC && row < nrows && s_off[row] >= 0)
+            *reinterpret_cast<uint4*>(s_ent + 16 * j) = v[k];
+    }
+    __syncthreads();
+
+    const int lane = lane_id(), w = wave_id();
+#pragma unroll
+    for (int i = 0; i < kGatherTile / kWavesPerBlock; i++) {
+        const int row = w + kWavesPerBlock * i;
+        if (row >= nrows) break;
+        const uint8_t* e = s_ent + row * EB;
+        uint4 o = make_uint4(0, 0, 0, 0);
+        if (s_off[row] >= 0) {
+            if (NVFP4) {                                 // values 8l..8l+7, block l/2
+                const uint32_t nib = *reinterpret_cast<const uint32_t*>(e + 4 * lane);
+                const float s = e4m3_f32(e[kNvScaleOff + (lane >> 1)]);
                 const f32x2 a = e2m1x2_f32<0>(nib), b = e2m1x2_f32<1>(nib);
                 const f32x2 c = e2m1x2_f32<2>(nib), d = e2m1x2_f32<3>(nib);
                 o = make_uint4(pack_bf16x2(a.x * s, a.y * s), pack_bf16x2(b.x * s, b.y * s),
                                pack_bf16x2(c.x * s, c.y * s), pack_bf16x2(d.x * s, d.y * s));
-            } else {
-                const float sc = __uint_as_float(a32[k]);
-                const f32x2 a = e4m3x2_f32<false>(a64[k].x), b = e4m3x2_f32<true>(a64[k].x);
-                const f32x2 c = e4m3x2_f32<false>(a64[k].y), d = e4m3x2_f32<true>(a64[k].y);
+            } else {                                     // values 8l..8l+7, group l/16
+                const uint2 q = *reinterpret_cast<const uint2*>(e + 8 * lane);
+                const float sc = *reinterpret_cast<const float*>(e + kF8ScaleOff + 4 * (lane >> 4));
+                const f32x2 a = e4m3x2_f32<false>(q.x), b = e4m3x2_f32<true>(q.x);
+                const f32x2 c = e4m3x2_f32<false>(q.y), d = e4m3x2_f32<true>(q.y);
                 o = make_uint4(pack_bf16x2(a.x * sc, a.y * sc), pack_bf16x2(b.x * sc, b.y * sc),
                                pack_bf16x2(c.x * sc, c.y * sc), pack_bf16x2(d.x * sc, d.y * sc));
             }
-            st_stream16(p.dst + (r0 + k) * p.dst_stride + 8 * lane, o);
         }
-        if (rk < nrows) {
-            uint4 o = rv;
+        st_stream16(p.dst + (r0 + row) * p.dst_stride + 8 * lane, o);
+    }
+    if (tid < nrows * 8) {                               // RoPE: 8 pieces of 8 values per row
+        const int row = tid >> 3, c = tid & 7;
+        const uint8_t* e = s_ent + row * EB;
+        uint4 o = make_uint4(0, 0, 0, 0);
+        if (s_off[row] >= 0) {
             if (NVFP4) {
-                const f32x2 a = e4m3x2_f32<false>(rv.x), b = e4m3x2_f32<true>(rv.x);
-                const f32x2 c = e4m3x2_f32<false>(rv.y), d = e4m3x2_f32<true>(rv.y);
-                o = make_uint4(pack_bf16x2(a.x, a.y), pack_bf16x2(b.x, b.y), pack_bf16x2(c.x, c.y),
+                const uint2 q = *reinterpret_cast<const uint2*>(e + kNvRopeOff + 8 * c);
+                const f32x2 a = e4m3x2_f32<false>(q.x), b = e4m3x2_f32<true>(q.x);
+                const f32x2 cc = e4m3x2_f32<false>(q.y), d = e4m3x2_f32<true>(q.y);
+                o = make_uint4(pack_bf16x2(a.x, a.y), pack_bf16x2(b.x, b.y), pack_bf16x2(cc.x, cc.y),
                                pack_bf16x2(d.x, d.y));
+            } else {
+                o = *reinterpret_cast<const uint4*>(e + kF8RopeOff + 16 * c);
             }
-            st_stream16(p.dst + (r0 + rk) * p.dst_stride + kNope + 8 * rc, o);
         }
+        st_stream16(p.dst + (r0 + row) * p.dst_stride + kNope + 8 * c, o);
     }
 }
 
@@ -285,10 +303,10 @@ hipError_t launch_write_fp8_ds_mla(const DsMlaWriteParams& p, hipStream_t s) {
     return launch_waves(k_write_fp8_ds_mla, (p.num_tokens + kF8TokPerWave - 1) / kF8TokPerWave, s, p);
 }
 hipError_t launch_gather_nvfp4_ds_mla(const DsMlaGatherParams& p, hipStream_t s) {
-    return launch_waves(k_gather_ds_mla<true>, (p.total + kRowsPerWave - 1) / kRowsPerWave, s, p);
+    return launch_groups(k_gather_ds_mla<true>, (p.total + kGatherTile - 1) / kGatherTile, s, p);
 }
 hipError_t launch_gather_fp8_ds_mla(const DsMlaGatherParams& p, hipStream_t s) {
-    return launch_waves(k_gather_ds_mla<false>, (p.total + kRowsPerWave - 1) / kRowsPerWave, s, p);
+    return launch_groups(k_gather_ds_mla<false>, (p.total + kGatherTile - 1) / kGatherTile, s, p);
 }
 
 }  // namespace gcache

@@ -79,6 +79,7 @@ int ds_write(bool nvfp4, const void* kv_c, const void* k_pe, void* kv_cache,
     p.cache = static_cast<uint8_t*>(kv_cache);
     p.slots = slot_mapping;
     p.num_tokens = num_tokens;
+    p.num_slots = num_blocks * block_size;
     p.kv_c_stride = kv_c_stride;
     p.k_pe_stride = k_pe_stride;
     p.block_stride = block_stride;
@@ -122,6 +123,7 @@ int ds_gather(bool nvfp4, const void* src_cache, void* dst, int64_t total_tokens
     p.ws = workspace_starts;
     p.seq_starts = seq_starts;
     p.batch = batch_size;
+    p.num_blocks = num_blocks;
     p.block_stride = block_stride;
     p.entry_stride = entry_stride;
     p.div = make_div(block_size);
@@ -141,7 +143,8 @@ int check_kv(int32_t num_heads, int32_t head_size, int64_t num_blocks, int32_t b
     for (int64_t x : v)
         if (x < 0) return GCACHE_ERR_SHAPE;
     int64_t tmp;
-    if (!mul_ok(num_blocks, L->block_stride, &tmp)) return GCACHE_ERR_SHAPE;
+    if (!mul_ok(num_blocks, L->block_stride, &tmp) || !mul_ok(num_blocks, block_size, &tmp))
+        return GCACHE_ERR_SHAPE;
     // data rows are read and written 8 (write) or 4 (gather) bytes at a time
     if (!aligned(cache, 16) || L->data_offset % 8 || L->data_token_stride % 8 ||
         L->data_head_stride % 8 || L->side_stride % 8 || L->block_stride % 8)
@@ -288,6 +291,7 @@ int gcache_reshape_and_cache_nvfp4(const void* key, const void* value, int64_t k
     p.cache = static_cast<uint8_t*>(kv_cache);
     p.slots = slot_mapping;
     p.num_tokens = num_tokens;
+    p.num_slots = num_blocks * block_size;
     p.num_heads = num_heads;
     p.head_size = head_size;
     p.bph_shift = log2_or_minus1(head_size / 16);
@@ -333,6 +337,7 @@ int gcache_gather_upconvert_nvfp4_kv(const void* kv_cache, void* key_out, void* 
     p.ws = workspace_starts;
     p.seq_starts = seq_starts;
     p.batch = batch_size;
+    p.num_blocks = num_blocks;
     p.num_heads = num_heads;
     p.head_size = head_size;
     p.cph_shift = log2_or_minus1(head_size / 8);

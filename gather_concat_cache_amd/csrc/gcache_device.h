@@ -130,12 +130,18 @@ __device__ __forceinline__ void st_stream1(void* p, uint8_t v) {
 
 // Split a slot (or logical position) into (block, offset).  `shift` >= 0
 // when block_size is a power of two.
+// A slot id outside [0, num_slots) -- padding (-1) or out of range -- is
+// skipped: it becomes -1.
+__device__ __forceinline__ int64_t valid_slot(int64_t slot, int64_t num_slots) {
+    return (uint64_t)slot < (uint64_t)num_slots ? slot : -1;
+}
+
 struct BlockDiv {
     int64_t size;
     int shift;
 };
-__device__ __forceinline__ void split_block(int64_t pos, const BlockDiv& d, int64_t& blk,
-                                            int64_t& off) {
+__host__ __device__ __forceinline__ void split_block(int64_t pos, const BlockDiv& d, int64_t& blk,
+                                                     int64_t& off) {
     if (d.shift >= 0) {
         blk = pos >> d.shift;
         off = pos & (d.size - 1);
@@ -167,18 +173,58 @@ __host__ __device__ __forceinline__ int find_request(const int32_t* __restrict__
     } else {
         hi = g;
         int step = 1;
-        lo = g - 1;                                // g >= 1 here since ws[0] == 0 <= r
-        while ((int64_t)ws[lo] > r) {
+        lo = g > 0 ? g - 1 : 0;
+        while (lo > 0 && (int64_t)ws[lo] > r) {
             hi = lo;
             step <<= 1;
             lo = (hi - step > 0) ? hi - step : 0;
         }
+        // Stopping at lo == 0 with ws[0] > r happens only when ws[0] != 0
+        // (invalid input): the result is then some request in [0, batch).
     }
     while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
         if ((int64_t)ws[mid] <= r) lo = mid; else hi = mid;
     }
     return lo;
+}
+
+// The same search for batch <= 64 as a fixed six-step bisection, so that all
+// lanes of a wave run identical steps; ws_at(i) returns ws[i] (on the device
+// a cross-lane read of the lane that holds it).  Returns the largest b in
+// [0, batch) with ws[b] <= r for non-decreasing ws with ws[0] == 0, and some
+// b in [0, batch) for any other ws.
+template <typename WsAt>
+__host__ __device__ __forceinline__ int bisect_request64(WsAt ws_at, int batch, int64_t r) {
+    int lo = 0, hi = batch;                        // lo <= mid < hi <= batch
+#pragma unroll
+    for (int it = 0; it < 6; it++) {
+        const int mid = (lo + hi) >> 1;
+        const int64_t wm = ws_at(mid);
+        if (hi - lo > 1) {
+            if (wm <= r) lo = mid;
+            else hi = mid;
+        }
+    }
+    return lo;
+}
+
+// Cache byte offset of the entry read by workspace row r of request b, or -1
+// when the row's position falls outside [0, bt_stride * block_size) or its
+// block id outside [0, num_blocks) (the kernels then write a zero row).
+__host__ __device__ __forceinline__ int64_t row_entry(const int32_t* __restrict__ block_table,
+                                                      int64_t bt_stride, int b, int64_t ws_b,
+                                                      int64_t seq_start_b, int64_t r,
+                                                      const BlockDiv& div, int64_t num_blocks,
+                                                      int64_t block_stride, int64_t entry_stride) {
+    const int64_t pos = seq_start_b + (r - ws_b);
+    if (pos < 0) return -1;
+    int64_t bi, off;
+    split_block(pos, div, bi, off);
+    if (bi >= bt_stride) return -1;
+    const int64_t blk = block_table[(int64_t)b * bt_stride + bi];
+    if (blk < 0 || blk >= num_blocks) return -1;
+    return blk * block_stride + off * entry_stride;
 }
 
 }  // namespace gcache

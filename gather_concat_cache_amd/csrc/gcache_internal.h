@@ -14,8 +14,9 @@ struct DsMlaWriteParams {
     const uint16_t* kv_c;        // bf16 [T, >=512]
     const uint16_t* k_pe;        // bf16 [T, >=64]
     uint8_t* cache;
-    const int64_t* slots;        // [T], < 0 = padding
+    const int64_t* slots;        // [T], outside [0, num_slots) = skipped (padding)
     int64_t num_tokens;
+    int64_t num_slots;           // num_blocks * block_size
     int64_t kv_c_stride, k_pe_stride;   // elements
     int64_t block_stride, entry_stride; // bytes
     BlockDiv div;                // block_size
@@ -30,6 +31,7 @@ struct DsMlaGatherParams {
     const int32_t* ws;           // workspace_starts [batch]
     const int32_t* seq_starts;   // [batch] or nullptr
     int32_t batch;
+    int64_t num_blocks;          // block ids outside [0, num_blocks): zero row
     int64_t block_stride, entry_stride;
     BlockDiv div;
 };
@@ -44,8 +46,9 @@ struct KvWriteParams {
     const uint16_t* src[2];      // key, value: bf16 [T, H, hs]
     int64_t token_stride[2], head_stride[2];  // elements
     uint8_t* cache;
-    const int64_t* slots;
+    const int64_t* slots;        // outside [0, num_slots) = skipped
     int64_t num_tokens;
+    int64_t num_slots;
     int32_t num_heads, head_size;
     int32_t bph_shift;           // log2(head_size / 16), or -1
     BlockDiv div;
@@ -63,6 +66,7 @@ struct KvGatherParams {
     const int32_t* ws;
     const int32_t* seq_starts;
     int32_t batch;
+    int64_t num_blocks;
     int32_t num_heads, head_size;
     int32_t cph_shift;           // log2(head_size / 8), or -1
     BlockDiv div;
@@ -89,6 +93,23 @@ inline hipError_t launch_waves(void (*kernel)(P, int64_t), int64_t waves, hipStr
         const int64_t nb = blocks - b0 < kMaxBlocks ? blocks - b0 : kMaxBlocks;
         int64_t wave0 = b0 * kWavesPerBlock;
         void* args[] = {const_cast<P*>(&p), &wave0};
+        const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3((unsigned)nb),
+                                             dim3(kBlockThreads), args, 0, s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+// Launch `groups` one-shot workgroups of `kernel(params, group0)`: the
+// kernel's workgroup index is group0 + blockIdx.x (pieces of at most 2^24
+// workgroups, as above).
+template <typename P>
+inline hipError_t launch_groups(void (*kernel)(P, int64_t), int64_t groups, hipStream_t s, const P& p) {
+    const int64_t kMaxBlocks = int64_t(1) << 24;
+    for (int64_t b0 = 0; b0 < groups; b0 += kMaxBlocks) {
+        const int64_t nb = groups - b0 < kMaxBlocks ? groups - b0 : kMaxBlocks;
+        int64_t group0 = b0;
+        void* args[] = {const_cast<P*>(&p), &group0};
         const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3((unsigned)nb),
                                              dim3(kBlockThreads), args, 0, s);
         if (e != hipSuccess) return e;

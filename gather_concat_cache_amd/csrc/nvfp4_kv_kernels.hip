@@ -38,7 +38,7 @@ __global__ __launch_bounds__(kBlockThreads) void k_reshape_and_cache_nvfp4(KvWri
     const int64_t t = wave0 + (int64_t)blockIdx.x * kWavesPerBlock + wave_id();
     if (t >= p.num_tokens) return;
     {
-        const int64_t slot = p.slots[t];
+        const int64_t slot = valid_slot(p.slots[t], p.num_slots);
         if (slot < 0) return;                             // padding token (wave-uniform)
         int64_t blk, off;
         split_block(slot, p.div, blk, off);
@@ -112,20 +112,24 @@ __global__ __launch_bounds__(kBlockThreads) void k_gather_nvfp4_kv(KvGatherParam
     const int nitems = 2 * nchunk;                       // both sides
     const int64_t r = wave0 + (int64_t)blockIdx.x * kWavesPerBlock + wave_id();
     if (r >= p.total) return;
-    // wave-uniform walk of row r
+    // wave-uniform walk of row r; blk < 0: the walk leaves the block table
+    // or the cache, and the row is written as zeros
     const int b = find_request(p.ws, p.batch, r, p.total);
     const int64_t pos = (p.seq_starts ? (int64_t)p.seq_starts[b] : 0) + (r - (int64_t)p.ws[b]);
-    int64_t bi, off;
-    split_block(pos, p.div, bi, off);
-    const int64_t blk = p.block_table[(int64_t)b * p.bt_stride + bi];
+    int64_t bi = -1, off = 0, blk = -1;
+    if (pos >= 0) split_block(pos, p.div, bi, off);
+    if (bi >= 0 && bi < p.bt_stride) {
+        blk = p.block_table[(int64_t)b * p.bt_stride + bi];
+        if (blk >= p.num_blocks) blk = -1;
+    }
     const float gs_k = *p.gscale[0], gs_v = *p.gscale[1];
 
     for (int base = 0; base < nitems; base += kKvGatherItems * kWave) {
-        uint32_t nib[kKvGatherItems], sfb[kKvGatherItems];
+        uint32_t nib[kKvGatherItems] = {}, sfb[kKvGatherItems] = {};
 #pragma unroll
         for (int u = 0; u < kKvGatherItems; u++) {       // all loads of the pass first
             const int it = base + u * kWave + lane;
-            if (it < nitems) {
+            if (it < nitems && blk >= 0) {
                 const int side = it >= nchunk;
                 int h, i;
                 split_pow2(it - side * nchunk, p.cph_shift, cph, h, i);   // values 8i..8i+7 of head h
@@ -148,10 +152,11 @@ __global__ __launch_bounds__(kBlockThreads) void k_gather_nvfp4_kv(KvGatherParam
             const f32x2 a = e2m1x2_f32<0>(nib[u]), bb = e2m1x2_f32<1>(nib[u]);
             const f32x2 cc = e2m1x2_f32<2>(nib[u]), d = e2m1x2_f32<3>(nib[u]);
             // (e2m1 * e4m3) is exact; one rounding for * gs, one for bf16.
-            const uint4 o = make_uint4(pack_bf16x2((a.x * s) * gs, (a.y * s) * gs),
-                                       pack_bf16x2((bb.x * s) * gs, (bb.y * s) * gs),
-                                       pack_bf16x2((cc.x * s) * gs, (cc.y * s) * gs),
-                                       pack_bf16x2((d.x * s) * gs, (d.y * s) * gs));
+            uint4 o = make_uint4(pack_bf16x2((a.x * s) * gs, (a.y * s) * gs),
+                                 pack_bf16x2((bb.x * s) * gs, (bb.y * s) * gs),
+                                 pack_bf16x2((cc.x * s) * gs, (cc.y * s) * gs),
+                                 pack_bf16x2((d.x * s) * gs, (d.y * s) * gs));
+            if (blk < 0) o = make_uint4(0, 0, 0, 0);
             st_stream16(p.out[side] + r * p.token_stride[side] + h * p.head_stride[side] + 8 * i, o);
         }
     }

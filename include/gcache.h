@@ -94,7 +94,10 @@ const char* gcache_status_string(int status);
  * laid out as [0,256) e2m1 NoPE (16 values -> 8 bytes at 8*j for block j),
  * [256,320) e4m3 RoPE, [320,352) the 32 e4m3 NoPE block scales (scale j at
  * byte 320 + j).  Tokens with slot < 0 are padding: nothing is read or
- * written for them.  Bytes outside the written entries are never touched.
+ * written for them; a slot id >= num_blocks * block_size is skipped the same
+ * way (never written out of the cache).  Bytes outside the written entries
+ * are never touched.  Two tokens with the same slot race (unspecified
+ * winner).
  *
  *  kv_c         bf16 [num_tokens, >=512], row stride kv_c_stride elements
  *  k_pe         bf16 [num_tokens, >=64],  row stride k_pe_stride elements
@@ -141,7 +144,11 @@ int gcache_cache_write_fp8_ds_mla(const void* kv_c, const void* k_pe, void* kv_c
  * empty requests are allowed).  It reads logical position
  *     p = seq_starts[b] + (r - workspace_starts[b])      (seq_starts NULL: 0)
  * of the request, i.e. the entry at offset p % block_size of cache block
- * block_table[b * block_table_stride + p / block_size], and writes
+ * block_table[b * block_table_stride + p / block_size] (workspace_starts must
+ * be non-decreasing with workspace_starts[0] = 0; for other values each row
+ * maps to some request in [0, batch_size).  A row with p < 0,
+ * p / block_size >= block_table_stride or a block id outside [0, num_blocks)
+ * reads nothing and is written as zeros), and writes
  *     dst[r, 0:512]   = bf16(e2m1 * e4m3 block scale)   (exact)
  *     dst[r, 512:576] = bf16(e4m3 RoPE)                  (exact)
  *
@@ -211,7 +218,8 @@ int gcache_nvfp4_kv_split_layout(int32_t block_size, int32_t num_heads, int32_t 
  * Per-head NVFP4 write (reshape_and_cache_nvfp4) -- [PR37332]
  * "Implementation breakdown" item 4.
  *
- * For every token t with slot >= 0 (block slot / block_size, offset
+ * For every token t with 0 <= slot < num_blocks * block_size (other slot
+ * ids are skipped, -1 being padding; block slot / block_size, offset
  * slot % block_size), side c in {K, V} with per-tensor scale gs (*k_scale or
  * *v_scale, device fp32 scalars > 0), head h and 16-value block j:
  *     sf = e4m3_rn_sat((amax / 6) / gs);  e = dec(sf) * gs;
@@ -242,6 +250,8 @@ int gcache_reshape_and_cache_nvfp4(const void* key, const void* value,
  * item 5).  Same walk as the DS-MLA gathers; for every workspace row r and
  * side c:
  *     out[r, h, i] = bf16_rne(binary32((e2m1 * e4m3 block scale) * gs))
+ * (rows whose walk leaves the block table or the cache are written as
+ * zeros, as in the DS-MLA gathers)
  *  key_out, value_out  bf16 [total_tokens, num_heads, head_size] with token
  *                      and head strides (elements; multiples of 8, bases
  *                      16-byte aligned)

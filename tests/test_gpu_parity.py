@@ -171,6 +171,82 @@ def test_full_size_prefill_write_and_gather(g, orc, fmt):
     run_ds_gather(orc, fmt, want, flat, gcase, gcase.num_blocks, gcase.block_size)
 
 
+@pytest.mark.parametrize("fmt", ["nvfp4", "fp8"])
+def test_request_counts_around_one_wave(g, orc, fmt):
+    """Batches of 1, 63, 64 and 65 requests (the gather resolves requests
+    with cross-lane reads up to 64 and searches memory beyond) and one
+    single-row request per token of the decode batch (4014 requests)."""
+    w = synth.config2()
+    want, flat = run_ds_write(orc, fmt, w.kv_c, w.k_pe, w.slot_mapping, w.num_blocks, w.block_size)
+    run_ds_gather(orc, fmt, want, flat, synth.per_token_gather("per-token", w.slot_mapping, w.num_blocks,
+                                                               w.block_size), w.num_blocks, w.block_size)
+    rng = np.random.default_rng(64)
+    for B in (1, 63, 64, 65):
+        gc_ = synth.prefill_gather(rng, f"B{B}", B, 1, 700, w.num_blocks, w.block_size, 12)
+        run_ds_gather(orc, fmt, want, flat, gc_, w.num_blocks, w.block_size)
+
+
+def _walk_slots(total, bt, ws, ss, bs, nb):
+    """Slot read by each workspace row (linear scan over the requests), -1
+    where the position leaves the block-table row or names a block outside
+    [0, nb)."""
+    out = np.full(total, -1, np.int64)
+    for r in range(total):
+        b = max(i for i in range(len(ws)) if ws[i] <= r)
+        pos = int(ss[b]) + r - int(ws[b])
+        if pos < 0 or pos // bs >= bt.shape[1]:
+            continue
+        blk = int(bt[b, pos // bs])
+        if 0 <= blk < nb:
+            out[r] = blk * bs + pos % bs
+    return out
+
+
+def _bad_metadata(nb, bs):
+    """Three requests over a 4-column block table: a block id past the cache,
+    a negative block id, and a request whose positions run past the row."""
+    bt = np.array([[0, 1, nb, 2], [3, -5, 4, 5], [5, 4, 3, 2]], np.int32)
+    ws = np.array([0, 57, 121], np.int32)
+    ss = np.array([3, 0, 50], np.int32)
+    return bt, ws, ss, 151
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "fp8"])
+def test_out_of_range_metadata(g, orc, fmt):
+    """Slot ids outside [0, num_blocks * block_size) are skipped like padding;
+    gather rows whose walk leaves the block-table row or the cache come back
+    as zeros and every other row is exact."""
+    eb, gwrite, ggather = _ds_pair(fmt)
+    _, ogather = _orc_ds(orc, fmt)
+    rng = np.random.default_rng(91)
+    nb, bs, T = 6, 16, 80
+    kv_c = synth.bf16_bits(rng.standard_normal((T, 512), dtype=np.float32))
+    k_pe = synth.bf16_bits(rng.standard_normal((T, 64), dtype=np.float32))
+    slots = rng.permutation(nb * bs)[:T].astype(np.int64)
+    raw = slots.copy()
+    raw[[3, 10, 40, 77]] = [nb * bs, -7, 1 << 40, nb * bs + 5]
+    clean = raw.copy()
+    clean[[3, 10, 40, 77]] = -1
+    want = np.full(nb * bs * eb, 0xA5, np.uint8)
+    _orc_ds(orc, fmt)[0](kv_c, k_pe, want, clean, nb, bs, bs * eb, eb)
+    flat = filled_cache((nb * bs * eb,), 0xA5)
+    gwrite(dev(kv_c), dev(k_pe), _cache_view(flat, nb, bs, bs * eb, eb), dev(raw))
+    torch.cuda.synchronize()
+    assert_same(host(flat), want, f"{fmt} write with out-of-range slots")
+
+    bt, ws, ss, total = _bad_metadata(nb, bs)
+    rs = _walk_slots(total, bt, ws, ss, bs, nb)
+    assert 0 < int((rs < 0).sum()) < total
+    exp = np.zeros((total, 576), np.uint16)
+    ok = rs >= 0
+    pt = synth.per_token_gather("valid rows", rs[ok], nb, bs)
+    exp[ok] = ogather(want, pt.total_tokens, pt.block_table, pt.workspace_starts, pt.seq_starts, nb, bs)
+    dst = dev(np.full((total, 576), 0x7FC1, np.uint16))
+    ggather(_cache_view(flat, nb, bs, bs * eb, eb), dst, dev(bt), dev(ws), dev(ss))
+    torch.cuda.synchronize()
+    assert_same(host(dst), exp, f"{fmt} gather with out-of-range metadata")
+
+
 # ---------------------------------------------------------------------------
 # per-head NVFP4 K/V
 # ---------------------------------------------------------------------------
@@ -256,3 +332,45 @@ def test_perhead_layouts(g, orc, variant):
         big2[:, :, :hs] = value
         vd = dev(big2)[:, :, :hs]
     run_kv(orc, g, key, value, slots, nb, bs, L_orc, L_gpu, ks, vs, kd, vd, out_hnd=(variant == "hnd"))
+
+
+def test_perhead_out_of_range_metadata(g, orc):
+    """Per-head write skips out-of-range slot ids; the per-head gather writes
+    zero K and V rows where the walk leaves the block table or the cache."""
+    rng = np.random.default_rng(92)
+    H, hs, nb, bs, T = 2, 64, 6, 16, 80
+    key, value, _ = _kv_case(rng, T, H, hs, nb, bs, 0)
+    slots = rng.permutation(nb * bs)[:T].astype(np.int64)
+    raw = slots.copy()
+    raw[[0, 33, 79]] = [nb * bs, -9, 1 << 41]
+    clean = raw.copy()
+    clean[[0, 33, 79]] = -1
+    ks, vs = synth.global_scale(key), synth.global_scale(value)
+    L = orc.kv_layout_split(bs, H, hs)
+    size = nb * L.block_stride
+    want = np.full(size, 0xA5, np.uint8)
+    orc.reshape_and_cache_nvfp4(key, value, want, clean, nb, bs, L, ks, vs)
+    flat = filled_cache((size,), 0xA5)
+    fd = hs // 2 + hs // 16
+    cache5 = torch.as_strided(flat, (nb, 2, bs, H, fd), (L.block_stride, L.side_stride, H * fd, fd, 1))
+    ks_d = torch.tensor([ks], dtype=torch.float32, device="cuda")
+    vs_d = torch.tensor([vs], dtype=torch.float32, device="cuda")
+    g.reshape_and_cache_nvfp4(dev(key), dev(value), cache5, dev(raw), ks_d, vs_d)
+    torch.cuda.synchronize()
+    assert_same(host(flat), want, "per-head write with out-of-range slots")
+
+    bt, ws, ss, total = _bad_metadata(nb, bs)
+    rs = _walk_slots(total, bt, ws, ss, bs, nb)
+    ok = rs >= 0
+    pt = synth.per_token_gather("valid rows", rs[ok], nb, bs)
+    vk, vv = orc.gather_upconvert_nvfp4_kv(want, pt.total_tokens, pt.block_table, pt.workspace_starts,
+                                           pt.seq_starts, H, hs, nb, bs, L, ks, vs)
+    ek = np.zeros((total, H, hs), np.uint16)
+    ev = np.zeros((total, H, hs), np.uint16)
+    ek[ok], ev[ok] = vk, vv
+    ko = dev(np.full((total, H, hs), 0x7FC1, np.uint16))
+    vo = dev(np.full((total, H, hs), 0x7FC1, np.uint16))
+    g.gather_upconvert_nvfp4_kv(cache5, ko, vo, dev(bt), dev(ws), ks_d, vs_d, seq_starts=dev(ss))
+    torch.cuda.synchronize()
+    assert_same(host(ko), ek, "per-head gather K with out-of-range metadata")
+    assert_same(host(vo), ev, "per-head gather V with out-of-range metadata")

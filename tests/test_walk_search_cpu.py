@@ -1,6 +1,9 @@
-"""Host check of the gather kernels' request search (interpolation guess,
-galloping, bisection) against a linear scan, on random workspace_starts with
-empty, one-row and long requests (tests/pins/walk_search.cpp)."""
+"""Host check of the gather kernels' request searches (interpolation guess,
+galloping, bisection; the six-step bisection used for batches up to 64)
+against a linear scan, on random workspace_starts with empty, one-row and
+long requests; termination inside [0, batch) on invalid workspace_starts; and
+the row-address bounds that turn a bad walk into a zero row
+(tests/pins/walk_search.cpp)."""
 import os
 import shutil
 import subprocess
@@ -10,7 +13,7 @@ import pytest
 from conftest import ROOT
 
 
-def test_find_request_matches_linear_scan(tmp_path):
+def test_request_search_and_row_bounds(tmp_path):
     hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(hipcc):
         pytest.skip("hipcc not available")
