@@ -8,20 +8,23 @@
 //
 // All four kernels are HBM-bound streams with no contraction.  What bounds
 // them on MI355X is latency (bytes in flight), the cache state left by the
-// previous op and the spread of the write front, so:
-//   - every wave is one-shot (one small group of tokens or rows, no
-//     grid-stride loop): the waves in flight then cover a compact, advancing
-//     window of addresses, which the memory system writes far faster than
-//     the scattered fronts of persistent loops;
+// previous op and the shape of the write front, so:
+//   - every workgroup is one-shot (one group of 16 tokens or rows, no
+//     grid-stride loop): the groups in flight then cover a compact,
+//     advancing window of addresses, which the memory system writes far
+//     faster than the scattered fronts of persistent loops;
 //   - every wave issues all of its loads before it needs them;
+//   - every store is a full 16-byte piece: the odd-sized parts of an entry
+//     (8-byte NoPE codes, scale bytes, 2-byte RoPE codes) are assembled in
+//     LDS first, so the cache sees whole 1 KiB runs instead of partial
+//     lines written by several instructions;
 //   - inputs and outputs use streaming (nontemporal) accesses.
 // Mappings:
 //   nvfp4 write : one lane per 16-value NoPE block (32 B in, 8 B + 1 scale
-//                 byte out), two tokens per half-wave pair, four tokens per
-//                 wave; no cross-lane reduction.
-//   fp8 write   : 8 values per lane (one 16 B load), one token per 64 lanes,
-//                 two tokens per wave; the 128-value group amax is a 4-step
-//                 DPP butterfly inside each 16-lane row.
+//                 byte staged), 32 lanes per token; no cross-lane reduction.
+//   fp8 write   : 8 values per lane (one 16 B load), one token per 64 lanes;
+//                 the 128-value group amax is a 4-step DPP butterfly inside
+//                 each 16-lane row.
 //   gathers     : one workgroup per 16 workspace rows; wave 0 resolves the
 //                 rows' cache addresses (batch <= 64: workspace_starts held
 //                 one per lane and bisected with cross-lane reads, then one
@@ -33,127 +36,162 @@
 namespace gcache {
 
 // ---------------------------------------------------------------------------
-// nvfp4_ds_mla write
+// writes: both formats quantize a group of kWriteTile tokens into an LDS
+// image of their entries, then store the entries as 16-byte pieces
 // ---------------------------------------------------------------------------
-constexpr int kNvTokPerWave = 4;   // two half-wave pairs
+constexpr int kWriteTile = 16;                       // tokens per workgroup
+constexpr int kTokPerWave = kWriteTile / kWavesPerBlock;
 
-__device__ __forceinline__ void nv_quantize_store(const DsMlaWriteParams& p, int64_t slot, uint4 v0,
-                                                  uint4 v1, uint32_t rw, int j) {
-    const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-    float x[16];
-#pragma unroll
-    for (int k = 0; k < 8; k++) {
-        x[2 * k] = bf16_lo(w[k]);
-        x[2 * k + 1] = bf16_hi(w[k]);
-    }
-    float amax = 0.0f;
-#pragma unroll
-    for (int k = 0; k < 16; k++) amax = fmaxf(amax, fabsf(x[k]));
-
-    // Block scale: e4m3_rn_sat(amax / 6), then the binary32 reciprocal of
-    // its decoded value (0 for a zero scale).
-    const uint32_t sf = put_e4m3x2<false>(0u, amax / 6.0f, 0.0f) & 0xFFu;
-    const float s = e4m3_f32(sf);
-    const float inv = (s == 0.0f) ? 0.0f : 1.0f / s;
-
-    uint32_t q0 = 0, q1 = 0;
-    q0 = put_e2m1x2<0>(q0, x[0] * inv, x[1] * inv);
-    q0 = put_e2m1x2<1>(q0, x[2] * inv, x[3] * inv);
-    q0 = put_e2m1x2<2>(q0, x[4] * inv, x[5] * inv);
-    q0 = put_e2m1x2<3>(q0, x[6] * inv, x[7] * inv);
-    q1 = put_e2m1x2<0>(q1, x[8] * inv, x[9] * inv);
-    q1 = put_e2m1x2<1>(q1, x[10] * inv, x[11] * inv);
-    q1 = put_e2m1x2<2>(q1, x[12] * inv, x[13] * inv);
-    q1 = put_e2m1x2<3>(q1, x[14] * inv, x[15] * inv);
-    const uint32_t rq = put_e4m3x2<false>(0u, bf16_lo(rw), bf16_hi(rw));
-
+// Cache byte offset of a slot's entry, -1 for a skipped slot.
+__device__ __forceinline__ int64_t slot_entry(const DsMlaWriteParams& p, int64_t slot) {
+    if (slot < 0) return -1;
     int64_t blk, off;
     split_block(slot, p.div, blk, off);
-    uint8_t* e = p.cache + blk * p.block_stride + off * p.entry_stride;
-    st_stream8(e + 8 * j, make_uint2(q0, q1));
-    st_stream2(e + kNvRopeOff + 2 * j, (uint16_t)rq);
-    st_stream1(e + kNvScaleOff + j, (uint8_t)sf);
+    return blk * p.block_stride + off * p.entry_stride;
 }
 
-__global__ __launch_bounds__(kBlockThreads) void k_write_nvfp4_ds_mla(DsMlaWriteParams p, int64_t wave0) {
-    const int lane = lane_id();
-    const int half = lane >> 5;   // token of the pair
-    const int j = lane & 31;      // NoPE block (values 16j .. 16j+15), RoPE pair j
-    const int64_t g = wave0 + (int64_t)blockIdx.x * kWavesPerBlock + wave_id();
-    if (g * kNvTokPerWave >= p.num_tokens) return;
-    int64_t slot[2];
-    uint4 v0[2], v1[2];
-    uint32_t rw[2];
+// Store the staged entries of the group: piece q = k * EC + j (entry k,
+// bytes 16j..16j+15) by thread q mod 256.  Consecutive slots make each
+// wave's store one contiguous 1 KiB run.
+template <int EB>
+__device__ __forceinline__ void store_staged(const DsMlaWriteParams& p, const uint8_t* s_ent,
+                                             const int64_t* s_addr) {
+    constexpr int EC = EB / 16;
 #pragma unroll
-    for (int k = 0; k < 2; k++) {
-        const int64_t t = g * kNvTokPerWave + 2 * k + half;
-        slot[k] = (t < p.num_tokens) ? valid_slot(p.slots[t], p.num_slots) : -1;
+    for (int q = threadIdx.x; q < kWriteTile * EC; q += kBlockThreads) {
+        const int k = q / EC;
+        const int64_t a = s_addr[k];
+        if (a >= 0) st_stream16(p.cache + a + 16 * (q - k * EC), *reinterpret_cast<const uint4*>(s_ent + 16 * q));
+    }
+}
+
+// nvfp4_ds_mla: lane j of each half-wave quantizes NoPE block j (values
+// 16j..16j+15) and RoPE pair j of one token; wave w stages tokens
+// w*kTokPerWave .. +kTokPerWave-1 of the group, two per pass.
+__global__ __launch_bounds__(kBlockThreads) void k_write_nvfp4_ds_mla(DsMlaWriteParams p, int64_t group0) {
+    constexpr int kPasses = kTokPerWave / 2;
+    __shared__ __align__(16) uint8_t s_ent[kWriteTile * kNvEntry];
+    __shared__ int64_t s_addr[kWriteTile];
+    const int lane = lane_id(), w = wave_id();
+    const int half = lane >> 5, j = lane & 31;
+    const int64_t t0 = (group0 + blockIdx.x) * kWriteTile;
+    if (t0 >= p.num_tokens) return;                      // workgroup-uniform
+
+    int64_t slot[kPasses];
+    uint4 v0[kPasses], v1[kPasses];
+    uint32_t rw[kPasses];
+#pragma unroll
+    for (int i = 0; i < kPasses; i++) {
+        const int64_t t = t0 + w * kTokPerWave + 2 * i + half;
+        slot[i] = t < p.num_tokens ? valid_slot(p.slots[t], p.num_slots) : -1;
     }
 #pragma unroll
-    for (int k = 0; k < 2; k++) {                        // padding tokens read nothing
-        if (slot[k] >= 0) {
-            const int64_t t = g * kNvTokPerWave + 2 * k + half;
-            const uint8_t* row = reinterpret_cast<const uint8_t*>(p.kv_c + t * p.kv_c_stride) + 32 * j;
-            v0[k] = ld_stream16(row);
-            v1[k] = ld_stream16(row + 16);
-            rw[k] = ld_stream4(reinterpret_cast<const uint8_t*>(p.k_pe + t * p.k_pe_stride) + 4 * j);
+    for (int i = 0; i < kPasses; i++) {                  // all loads first; padding reads nothing
+        if (slot[i] < 0) continue;
+        const int64_t t = t0 + w * kTokPerWave + 2 * i + half;
+        const uint8_t* row = reinterpret_cast<const uint8_t*>(p.kv_c + t * p.kv_c_stride) + 32 * j;
+        v0[i] = ld_stream16(row);
+        v1[i] = ld_stream16(row + 16);
+        rw[i] = ld_stream4(reinterpret_cast<const uint8_t*>(p.k_pe + t * p.k_pe_stride) + 4 * j);
+    }
+#pragma unroll
+    for (int i = 0; i < kPasses; i++) {
+        const int k = w * kTokPerWave + 2 * i + half;
+        if (j == 0) s_addr[k] = slot_entry(p, slot[i]);
+        if (slot[i] < 0) continue;
+        const uint32_t wv[8] = {v0[i].x, v0[i].y, v0[i].z, v0[i].w, v1[i].x, v1[i].y, v1[i].z, v1[i].w};
+        float x[16];
+#pragma unroll
+        for (int q = 0; q < 8; q++) {
+            x[2 * q] = bf16_lo(wv[q]);
+            x[2 * q + 1] = bf16_hi(wv[q]);
         }
-    }
+        float amax = 0.0f;
 #pragma unroll
-    for (int k = 0; k < 2; k++)
-        if (slot[k] >= 0) nv_quantize_store(p, slot[k], v0[k], v1[k], rw[k], j);
+        for (int q = 0; q < 16; q++) amax = fmaxf(amax, fabsf(x[q]));
+        // Block scale: e4m3_rn_sat(amax / 6), then the binary32 reciprocal
+        // of its decoded value (0 for a zero scale).
+        const uint32_t sf = put_e4m3x2<false>(0u, amax / 6.0f, 0.0f) & 0xFFu;
+        const float s = e4m3_f32(sf);
+        const float inv = (s == 0.0f) ? 0.0f : 1.0f / s;
+        uint32_t q0 = 0, q1 = 0;
+        q0 = put_e2m1x2<0>(q0, x[0] * inv, x[1] * inv);
+        q0 = put_e2m1x2<1>(q0, x[2] * inv, x[3] * inv);
+        q0 = put_e2m1x2<2>(q0, x[4] * inv, x[5] * inv);
+        q0 = put_e2m1x2<3>(q0, x[6] * inv, x[7] * inv);
+        q1 = put_e2m1x2<0>(q1, x[8] * inv, x[9] * inv);
+        q1 = put_e2m1x2<1>(q1, x[10] * inv, x[11] * inv);
+        q1 = put_e2m1x2<2>(q1, x[12] * inv, x[13] * inv);
+        q1 = put_e2m1x2<3>(q1, x[14] * inv, x[15] * inv);
+        const uint32_t rq = put_e4m3x2<false>(0u, bf16_lo(rw[i]), bf16_hi(rw[i]));
+        uint8_t* e = s_ent + k * kNvEntry;
+        *reinterpret_cast<uint2*>(e + 8 * j) = make_uint2(q0, q1);
+        *reinterpret_cast<uint16_t*>(e + kNvRopeOff + 2 * j) = (uint16_t)rq;
+        e[kNvScaleOff + j] = (uint8_t)sf;
+    }
+    __syncthreads();
+    store_staged<kNvEntry>(p, s_ent, s_addr);
 }
-
-// ---------------------------------------------------------------------------
-// fp8_ds_mla write: 512 e4m3 | 4 x fp32 scale (amax / 448 per 128) | 64 bf16
-// ---------------------------------------------------------------------------
-constexpr int kF8TokPerWave = 2;
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float v) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 
-__global__ __launch_bounds__(kBlockThreads) void k_write_fp8_ds_mla(DsMlaWriteParams p, int64_t wave0) {
-    const int lane = lane_id();
-    const int64_t t0 = (wave0 + (int64_t)blockIdx.x * kWavesPerBlock + wave_id()) * kF8TokPerWave;
-    if (t0 >= p.num_tokens) return;
-    int64_t slot[kF8TokPerWave];                         // wave-uniform
+// fp8_ds_mla: 512 e4m3 | 4 x fp32 scale (amax / 448 per 128) | 64 bf16.
+// Wave w stages tokens w, w+4, ... of the group, one token per 64 lanes
+// (8 values per lane); the 128-value group amax is a 4-step DPP butterfly
+// inside each 16-lane row.  RoPE: lanes 8i..8i+7 copy token w+4i's 128 B.
+__global__ __launch_bounds__(kBlockThreads) void k_write_fp8_ds_mla(DsMlaWriteParams p, int64_t group0) {
+    static_assert(kTokPerWave <= 8, "RoPE copy uses 8 lanes per token");
+    __shared__ __align__(16) uint8_t s_ent[kWriteTile * kF8Entry];
+    __shared__ int64_t s_addr[kWriteTile];
+    const int lane = lane_id(), w = wave_id();
+    const int64_t t0 = (group0 + blockIdx.x) * kWriteTile;
+    if (t0 >= p.num_tokens) return;                      // workgroup-uniform
+
+    int64_t slot[kTokPerWave];                           // wave-uniform
+    uint4 v[kTokPerWave];
 #pragma unroll
-    for (int k = 0; k < kF8TokPerWave; k++)
-        slot[k] = (t0 + k < p.num_tokens) ? valid_slot(p.slots[t0 + k], p.num_slots) : -1;
-    uint4 v[kF8TokPerWave];
+    for (int i = 0; i < kTokPerWave; i++) {
+        const int64_t t = t0 + w + kWavesPerBlock * i;
+        slot[i] = t < p.num_tokens ? valid_slot(p.slots[t], p.num_slots) : -1;
+    }
 #pragma unroll
-    for (int k = 0; k < kF8TokPerWave; k++)
-        if (slot[k] >= 0)
-            v[k] = ld_stream16(reinterpret_cast<const uint8_t*>(p.kv_c + (t0 + k) * p.kv_c_stride) + 16 * lane);
-    // RoPE (128 B bf16 per token): 8 lanes x 16 B per token, copied as is.
-    const int rk = (lane >> 3) & (kF8TokPerWave - 1), rc = lane & 7;
-    const int64_t rslot = rk == 0 ? slot[0] : slot[1];
-    const bool rope_lane = lane < 8 * kF8TokPerWave && rslot >= 0;
+    for (int i = 0; i < kTokPerWave; i++)
+        if (slot[i] >= 0)
+            v[i] = ld_stream16(reinterpret_cast<const uint8_t*>(
+                                   p.kv_c + (t0 + w + kWavesPerBlock * i) * p.kv_c_stride) + 16 * lane);
+    const int ri = lane >> 3, rc = lane & 7;
+    int64_t rslot = -1;
+#pragma unroll
+    for (int i = 0; i < kTokPerWave; i++)
+        if (ri == i) rslot = slot[i];
     uint4 r = make_uint4(0, 0, 0, 0);
-    if (rope_lane)
-        r = ld_stream16(reinterpret_cast<const uint8_t*>(p.k_pe + (t0 + rk) * p.k_pe_stride) + 16 * rc);
+    if (rslot >= 0)
+        r = ld_stream16(reinterpret_cast<const uint8_t*>(
+                            p.k_pe + (t0 + w + kWavesPerBlock * ri) * p.k_pe_stride) + 16 * rc);
 
 #pragma unroll
-    for (int k = 0; k < kF8TokPerWave; k++) {
-        if (slot[k] < 0) continue;                       // wave-uniform: DPP below sees all lanes
-        const uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+    for (int i = 0; i < kTokPerWave; i++) {
+        const int k = w + kWavesPerBlock * i;
+        if (lane == 0) s_addr[k] = slot_entry(p, slot[i]);
+        if (slot[i] < 0) continue;                       // wave-uniform: DPP below sees all lanes
+        const uint32_t wv[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
         float x[8];
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            x[2 * i] = bf16_lo(w[i]);
-            x[2 * i + 1] = bf16_hi(w[i]);
+        for (int q = 0; q < 4; q++) {
+            x[2 * q] = bf16_lo(wv[q]);
+            x[2 * q + 1] = bf16_hi(wv[q]);
         }
         float amax = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 8; i++) amax = fmaxf(amax, fabsf(x[i]));
+        for (int q = 0; q < 8; q++) amax = fmaxf(amax, fabsf(x[q]));
         // 16 lanes x 8 values = one 128-value group: butterfly max in the row.
         amax = fmaxf(amax, dpp_f32<0xB1>(amax));    // quad_perm [1,0,3,2]
         amax = fmaxf(amax, dpp_f32<0x4E>(amax));    // quad_perm [2,3,0,1]
         amax = fmaxf(amax, dpp_f32<0x141>(amax));   // row_half_mirror
         amax = fmaxf(amax, dpp_f32<0x140>(amax));   // row_mirror
-
         const float sc = amax / 448.0f;
         const float inv = (sc == 0.0f) ? 0.0f : 1.0f / sc;
         uint32_t q0 = 0, q1 = 0;
@@ -161,18 +199,14 @@ __global__ __launch_bounds__(kBlockThreads) void k_write_fp8_ds_mla(DsMlaWritePa
         q0 = put_e4m3x2<true>(q0, x[2] * inv, x[3] * inv);
         q1 = put_e4m3x2<false>(q1, x[4] * inv, x[5] * inv);
         q1 = put_e4m3x2<true>(q1, x[6] * inv, x[7] * inv);
-
-        int64_t blk, off;
-        split_block(slot[k], p.div, blk, off);
-        uint8_t* e = p.cache + blk * p.block_stride + off * p.entry_stride;
-        st_stream8(e + 8 * lane, make_uint2(q0, q1));
-        if ((lane & 15) == 0) st_stream4(e + kF8ScaleOff + 4 * (lane >> 4), __float_as_uint(sc));
+        uint8_t* e = s_ent + k * kF8Entry;
+        *reinterpret_cast<uint2*>(e + 8 * lane) = make_uint2(q0, q1);
+        if ((lane & 15) == 0) *reinterpret_cast<float*>(e + kF8ScaleOff + 4 * (lane >> 4)) = sc;
     }
-    if (rope_lane) {
-        int64_t blk, off;
-        split_block(rslot, p.div, blk, off);
-        st_stream16(p.cache + blk * p.block_stride + off * p.entry_stride + kF8RopeOff + 16 * rc, r);
-    }
+    if (rslot >= 0)
+        *reinterpret_cast<uint4*>(s_ent + (w + kWavesPerBlock * ri) * kF8Entry + kF8RopeOff + 16 * rc) = r;
+    __syncthreads();
+    store_staged<kF8Entry>(p, s_ent, s_addr);
 }
 
 // ---------------------------------------------------------------------------
@@ -297,10 +331,10 @@ __global__ __launch_bounds__(kBlockThreads) void k_gather_ds_mla(DsMlaGatherPara
 // launchers
 // ---------------------------------------------------------------------------
 hipError_t launch_write_nvfp4_ds_mla(const DsMlaWriteParams& p, hipStream_t s) {
-    return launch_waves(k_write_nvfp4_ds_mla, (p.num_tokens + kNvTokPerWave - 1) / kNvTokPerWave, s, p);
+    return launch_groups(k_write_nvfp4_ds_mla, (p.num_tokens + kWriteTile - 1) / kWriteTile, s, p);
 }
 hipError_t launch_write_fp8_ds_mla(const DsMlaWriteParams& p, hipStream_t s) {
-    return launch_waves(k_write_fp8_ds_mla, (p.num_tokens + kF8TokPerWave - 1) / kF8TokPerWave, s, p);
+    return launch_groups(k_write_fp8_ds_mla, (p.num_tokens + kWriteTile - 1) / kWriteTile, s, p);
 }
 hipError_t launch_gather_nvfp4_ds_mla(const DsMlaGatherParams& p, hipStream_t s) {
     return launch_groups(k_gather_ds_mla<true>, (p.total + kGatherTile - 1) / kGatherTile, s, p);
