@@ -53,6 +53,11 @@ def parse():
     ap.add_argument("--traffic-from", nargs=2, default=None, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="host only: turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then "
                          "WRITE_SIZE, each with --copy-calibration) into profiles/traffic.json")
+    ap.add_argument("--stats-from", default=None, metavar="PROF_DIR",
+                    help="host only: turn a rocprofv3 --kernel-trace --stats run of this script "
+                         "(--steps 20 --warmup 3) into profiles/prefill_pass_all_kernels_stats.md")
+    ap.add_argument("--bench-json", default=None, metavar="FILE",
+                    help="with --stats-from: a bench.py output line of the same build, tabulated beside")
     return ap.parse_args()
 
 
@@ -93,6 +98,9 @@ def main():
     args = parse()
     if args.traffic_from:
         write_traffic(*args.traffic_from)
+        return
+    if args.stats_from:
+        write_stats(args.stats_from, args.bench_json)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
@@ -328,7 +336,65 @@ def write_traffic(fetch_dir, write_dir):
     with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")
+    cal_f = ", ".join(f"{v:,.0f}" for v in fetch["calibration"])
+    cal_w = ", ".join(f"{v:,.0f}" for v in write["calibration"])
+    run = ("timeout -s KILL 120 rocprofv3 --pmc {c} --kernel-trace -f csv -d $R/{d} -o bench -- python3 "
+           "$R/bench.py --steps 3 --warmup 1 --no-cpu-baseline --copy-calibration 1024")
+    md = ["# HBM traffic per launch — all six kernels, prefill-context pass workload", "",
+          "Two counter runs (one counter each), from /tmp on the MI355X box with the repository at $R, "
+          "then the host-side summary:", "", "```",
+          run.format(c="FETCH_SIZE", d=os.path.relpath(fetch_dir, ROOT)),
+          run.format(c="WRITE_SIZE", d=os.path.relpath(write_dir, ROOT)),
+          f"python3 bench.py --traffic-from {os.path.relpath(fetch_dir, ROOT)} "
+          f"{os.path.relpath(write_dir, ROOT)}", "```", "",
+          f"Kernel sources: library digest {out['source_digest']}. Calibration: torch's elementwise add "
+          f"over {cal_mib} MiB (reads and writes {cal_kib:,.0f} KiB each); FETCH_SIZE read {cal_f} KiB "
+          f"and WRITE_SIZE {cal_w} KiB per dispatch, so fetch counts are scaled by {out['fetch_scale']} "
+          f"and write counts by {out['write_scale']}. Each kernel: mean over its dispatches "
+          "(1 warm-up + 3 timed steps).", "",
+          "| Kernel op | FETCH_SIZE (KiB, raw) | WRITE_SIZE (KiB, raw) | HBM bytes / launch (scaled) "
+          "| Algorithmic bytes | Ratio |", "|---|---|---|---|---|---|"]
+    for k, v in out["kernels"].items():
+        md.append(f"| {k} | {v['fetch_kib_raw']:,} | {v['write_kib_raw']:,} | {v['hbm_bytes_per_launch']:,} "
+                  f"| {v['algorithmic_bytes']:,} | {v['traffic_over_algorithmic']:.4f} |")
+    md += ["", "Kernel symbols: " + ", ".join(f"{op} = `{k}`" for k, op in KERNEL_OPS.items()) + "."]
+    with open(os.path.join(ROOT, "profiles", "all_kernels_hbm_traffic_pmc.md"), "w") as f:
+        f.write("\n".join(md) + "\n")
     print(json.dumps(out, indent=1))
+
+
+def write_stats(prof_dir, bench_json):
+    """Markdown summary of a rocprofv3 --stats run of this script, with the
+    HIP-event figures of a bench.py line of the same build when given."""
+    import csv
+    import glob
+    from gather_concat_cache_amd.build import source_digest
+    (path,) = glob.glob(os.path.join(prof_dir, "*kernel_stats.csv"))
+    rows = list(csv.DictReader(open(path)))
+    cmd = ("rocprofv3 --kernel-trace --stats -f csv -d $R/" + os.path.relpath(prof_dir, ROOT) +
+           " -o bench -- python3 $R/bench.py --steps 20 --warmup 3 --no-cpu-baseline")
+    md = ["# rocprofv3 kernel statistics — all six kernels, prefill-context pass workload", "",
+          "Command (from /tmp on the MI355X box, repository at $R), then the host-side summary:", "",
+          "```", cmd, f"python3 bench.py --stats-from {os.path.relpath(prof_dir, ROOT)}"
+          + (f" --bench-json {os.path.relpath(bench_json, ROOT)}" if bench_json else ""), "```", "",
+          "20 timed + 3 warm-up steps (23 calls per kernel). Workloads: nvfp4_ds_mla write 524288 tokens, "
+          "fp8_ds_mla write 1048576 tokens, nvfp4 gather 161766 rows, fp8 gather 219273 rows, per-head "
+          f"write 8192 tokens x 8 heads x 128, per-head gather 8110 rows. Library digest {source_digest()}.",
+          "", "| Kernel | Calls | Average (ns) | Min (ns) | Max (ns) | % of GPU time |",
+          "|---|---|---|---|---|---|"]
+    for r in rows:
+        n = r["Name"] if len(r["Name"]) <= 72 else r["Name"][:72] + "…"
+        md.append(f"| `{n}` | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | {r['MaxNs']} "
+                  f"| {float(r['Percentage']):.2f} |")
+    if bench_json:
+        b = json.load(open(bench_json))
+        md += ["", f"Same-build HIP-event averages from `python bench.py` ({b['steps']} timed steps; "
+               f"whole step {b['value']} GB/s, {100 * b['frac_of_hbm_peak']:.1f} % of 8 TB/s):", "",
+               "| Kernel op | ms | GB/s | % of 8 TB/s |", "|---|---|---|---|"]
+        for k, v in b["kernels"].items():
+            md.append(f"| {k} | {v['ms']:.5f} | {v['GB_per_s']:.0f} | {100 * v['frac_of_hbm_peak']:.1f} |")
+    with open(os.path.join(ROOT, "profiles", "prefill_pass_all_kernels_stats.md"), "w") as f:
+        f.write("\n".join(md) + "\n")
 
 
 # ---------------------------------------------------------------------------
