@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--cold", action="store_true",
                     help="also time every kernel once per run after evicting the caches")
     ap.add_argument("--only", default=None, help="comma list of op names to run (profiling aid)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the comparator measured after the timed step (BF16 gather)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run a plain elementwise kernel reading and writing MIB MiB, three "
                          "times, outside the timed region, so HBM counters can be scaled against "
@@ -193,6 +195,8 @@ def main():
                          "GB_per_s": round(nbytes / (ms * 1e6), 1),
                          "frac_of_hbm_peak": round(nbytes / (ms * 1e6) / HBM_PEAK_GBS, 4)}
 
+    extras = None if args.no_extras else measure_extras(torch, gc, g3, args.steps, dev_arr)
+
     if args.copy_calibration:
         # a plain elementwise kernel that reads and writes exactly n bytes each
         # (torch's copy_ of two device buffers goes to a DMA engine instead)
@@ -232,11 +236,43 @@ def main():
         "kernels": kernels,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "extras": extras,
         "input_generation_s": round(gen_s, 2),
     }
     if cold is not None:
         out["kernels_cold"] = cold
     print(json.dumps(out), flush=True)
+
+
+def measure_extras(torch, gc, g3, steps, dev_arr):
+    """Outside the timed step: the BF16 comparator gather (same walk, 1152-byte
+    bf16 entries copied) over the nvfp4 prefill gather's requests and cache
+    geometry -- what a walk-driven gather of full rows reaches on this device.
+    HIP events around each launch on the launch stream, mean over `steps`."""
+    import synth
+    nb, bs = g3.num_blocks, g3.block_size
+    cache = torch.from_numpy(synth.normal_bf16_rows(1013, 0, nb * bs, 576).view(np.int16)) \
+        .view(torch.bfloat16).reshape(nb, bs, 576).cuda()
+    dst = torch.empty((g3.total_tokens, 576), dtype=torch.bfloat16, device="cuda")
+    bt, ws, ss = dev_arr(g3.block_table), dev_arr(g3.workspace_starts), dev_arr(g3.seq_starts)
+    run = lambda: gc.cache_gather_bf16(cache, dst, bt, ws, ss)
+    for _ in range(3):
+        run()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in ev:
+        a.record()
+        run()
+        b.record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    nbytes = g3.total_tokens * 2 * 1152
+    del cache, dst
+    return {"bf16_gather_comparator": {
+        "ms": round(ms, 5), "bytes": nbytes, "units": g3.total_tokens,
+        "GB_per_s": round(nbytes / (ms * 1e6), 1), "frac_of_hbm_peak": round(nbytes / (ms * 1e6) / HBM_PEAK_GBS, 4),
+        "rows_per_s": round(g3.total_tokens / (ms * 1e-3), 1),
+        "workload": f"{g3.total_tokens} rows of the nvfp4 prefill gather over a bf16 cache "
+                    f"{nb} x {bs} x 1152 B (1152 B read + 1152 B written per row)"}}
 
 
 def measure_cold(torch, ops, reps=5):

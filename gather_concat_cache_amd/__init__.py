@@ -7,7 +7,7 @@ memory and streams) into those calls.  Python names are the C names without
 the ``gcache_`` prefix.
 """
 from ._native import (FP8_DS_MLA, LIB_PATH, NVFP4_DS_MLA, GcacheError, NvFp4KvLayout,
-                      cache_gather_upconvert_fp8_ds_mla, cache_gather_upconvert_nvfp4_ds_mla,
+                      cache_gather_bf16, cache_gather_upconvert_fp8_ds_mla, cache_gather_upconvert_nvfp4_ds_mla,
                       cache_write_fp8_ds_mla, cache_write_nvfp4_ds_mla, entry_bytes,
                       gather_upconvert_nvfp4_kv, load, nvfp4_full_dim, nvfp4_kv_split_layout,
                       reshape_and_cache_nvfp4)
@@ -16,7 +16,7 @@ __all__ = [
     "NVFP4_DS_MLA", "FP8_DS_MLA", "LIB_PATH", "GcacheError", "NvFp4KvLayout", "load",
     "entry_bytes", "nvfp4_full_dim", "nvfp4_kv_split_layout",
     "cache_write_nvfp4_ds_mla", "cache_write_fp8_ds_mla",
-    "cache_gather_upconvert_nvfp4_ds_mla", "cache_gather_upconvert_fp8_ds_mla",
+    "cache_gather_upconvert_nvfp4_ds_mla", "cache_gather_upconvert_fp8_ds_mla", "cache_gather_bf16",
     "reshape_and_cache_nvfp4", "gather_upconvert_nvfp4_kv",
 ]
 

@@ -46,6 +46,8 @@ _SIGS = {
                                                             _I32, _I64, _I64, _P]),
     "gcache_cache_gather_upconvert_fp8_ds_mla": (C.c_int, [_P, _P, _I64, _I64, _P, _I64, _P, _P, _I32, _I64,
                                                           _I32, _I64, _I64, _P]),
+    "gcache_cache_gather_bf16": (C.c_int, [_P, _P, _I64, _I64, _P, _I64, _P, _P, _I32, _I64, _I32, _I64,
+                                           _I64, _P]),
     "gcache_nvfp4_kv_split_layout": (C.c_int, [_I32, _I32, _I32, C.POINTER(NvFp4KvLayout)]),
     "gcache_reshape_and_cache_nvfp4": (C.c_int, [_P, _P, _I64, _I64, _I64, _I64, _P, _P, _I64, _I32, _I32, _I64,
                                                  _I32, C.POINTER(NvFp4KvLayout), _P, _P, _P]),
@@ -196,6 +198,17 @@ def cache_gather_upconvert_fp8_ds_mla(src_cache, dst, block_table, workspace_sta
     """fp8_ds_mla gather-upconvert into dst bf16 [total_tokens, 576]."""
     _ds_gather("gcache_cache_gather_upconvert_fp8_ds_mla", src_cache, dst, block_table,
                workspace_starts, seq_starts, batch_size, stream)
+
+
+def cache_gather_bf16(src_cache, dst, block_table, workspace_starts, seq_starts=None, batch_size=None,
+                      stream=None):
+    """BF16 comparator: the same walk over a bf16 cache [num_blocks, block_size,
+    >=576] (unit last stride), rows copied into dst bf16 [total_tokens, 576]."""
+    if not isinstance(src_cache, torch.Tensor) or src_cache.dtype != torch.bfloat16 \
+            or src_cache.dim() != 3 or src_cache.stride(2) != 1:
+        raise ValueError("src_cache must be a bf16 [num_blocks, block_size, >=576] tensor with unit last stride")
+    _ds_gather("gcache_cache_gather_bf16", src_cache.view(torch.uint8), dst, block_table, workspace_starts,
+               seq_starts, batch_size, stream)
 
 
 # ---------------------------------------------------------------------------

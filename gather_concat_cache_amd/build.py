@@ -1,6 +1,6 @@
 """Build libgcache.so (HIP, gfx950 only) in-tree with hipcc.
 
-    python -m gather_concat_cache_amd.build [-v]
+    python gather_concat_cache_amd/build.py [-v]
 
 Flags:
   --offload-arch=gfx950            the only target

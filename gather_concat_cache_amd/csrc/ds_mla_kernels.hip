@@ -327,6 +327,42 @@ __global__ __launch_bounds__(kBlockThreads) void k_gather_ds_mla(DsMlaGatherPara
     }
 }
 
+// BF16 comparator: the same tile walk over a cache whose 1152-byte entries
+// hold the row's 576 bf16 values; each 16-byte piece is copied straight from
+// the cache to the workspace (all loads of the tile first, no LDS).
+constexpr int kBf16Entry = 2 * (kNope + kRope);
+constexpr int kBf16Pieces = kBf16Entry / 16;           // 72 per row
+
+__global__ __launch_bounds__(kBlockThreads) void k_gather_bf16(DsMlaGatherParams p, int64_t tile0) {
+    constexpr int kPieces = (kGatherTile * kBf16Pieces + kBlockThreads - 1) / kBlockThreads;
+    __shared__ int64_t s_off[kGatherTile];
+    const int tid = threadIdx.x;
+    const int64_t r0 = (tile0 + blockIdx.x) * kGatherTile;
+    if (r0 >= p.total) return;                           // workgroup-uniform
+    const int nrows = (int)min((int64_t)kGatherTile, p.total - r0);
+    if (tid < kWave) {
+        const int64_t e = tile_row_entry(p, r0, nrows, tid);
+        if (tid < kGatherTile) s_off[tid] = e;
+    }
+    __syncthreads();
+    uint4 v[kPieces];
+#pragma unroll
+    for (int k = 0; k < kPieces; k++) {
+        const int j = tid + kBlockThreads * k;
+        const int row = j / kBf16Pieces;
+        v[k] = make_uint4(0, 0, 0, 0);
+        if (j < kGatherTile * kBf16Pieces && row < nrows && s_off[row] >= 0)
+            v[k] = ld_stream16(p.cache + s_off[row] + 16 * (j - row * kBf16Pieces));
+    }
+#pragma unroll
+    for (int k = 0; k < kPieces; k++) {
+        const int j = tid + kBlockThreads * k;
+        const int row = j / kBf16Pieces;
+        if (j < kGatherTile * kBf16Pieces && row < nrows)
+            st_stream16(p.dst + (r0 + row) * p.dst_stride + 8 * (j - row * kBf16Pieces), v[k]);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
@@ -341,6 +377,9 @@ hipError_t launch_gather_nvfp4_ds_mla(const DsMlaGatherParams& p, hipStream_t s)
 }
 hipError_t launch_gather_fp8_ds_mla(const DsMlaGatherParams& p, hipStream_t s) {
     return launch_groups(k_gather_ds_mla<false>, (p.total + kGatherTile - 1) / kGatherTile, s, p);
+}
+hipError_t launch_gather_bf16(const DsMlaGatherParams& p, hipStream_t s) {
+    return launch_groups(k_gather_bf16, (p.total + kGatherTile - 1) / kGatherTile, s, p);
 }
 
 }  // namespace gcache

@@ -97,7 +97,9 @@ int check_walk(int64_t total_tokens, const int32_t* block_table, int64_t block_t
     return GCACHE_OK;
 }
 
-int ds_gather(bool nvfp4, const void* src_cache, void* dst, int64_t total_tokens,
+enum { kFmtNvfp4, kFmtFp8, kFmtBf16 };
+
+int ds_gather(int fmt, const void* src_cache, void* dst, int64_t total_tokens,
               int64_t dst_stride, const int32_t* block_table, int64_t block_table_stride,
               const int32_t* workspace_starts, const int32_t* seq_starts, int32_t batch_size,
               int64_t num_blocks, int32_t block_size, int64_t block_stride, int64_t entry_stride,
@@ -109,7 +111,7 @@ int ds_gather(bool nvfp4, const void* src_cache, void* dst, int64_t total_tokens
     if (rc) return rc;
     if (dst_stride < kRow) return GCACHE_ERR_SHAPE;
     if ((rc = check_ds_cache(src_cache, num_blocks, block_size, block_stride, entry_stride,
-                             nvfp4 ? kNvEntry : kF8Entry)))
+                             fmt == kFmtNvfp4 ? kNvEntry : fmt == kFmtFp8 ? kF8Entry : 2 * kRow)))
         return rc;
     if (!aligned(dst, 16) || dst_stride % 8) return GCACHE_ERR_ALIGN;
     if ((rc = check_device())) return rc;
@@ -127,7 +129,9 @@ int ds_gather(bool nvfp4, const void* src_cache, void* dst, int64_t total_tokens
     p.block_stride = block_stride;
     p.entry_stride = entry_stride;
     p.div = make_div(block_size);
-    return launched(nvfp4 ? launch_gather_nvfp4_ds_mla(p, stream) : launch_gather_fp8_ds_mla(p, stream));
+    return launched(fmt == kFmtNvfp4 ? launch_gather_nvfp4_ds_mla(p, stream)
+                    : fmt == kFmtFp8 ? launch_gather_fp8_ds_mla(p, stream)
+                                     : launch_gather_bf16(p, stream));
 }
 
 int check_kv(int32_t num_heads, int32_t head_size, int64_t num_blocks, int32_t block_size,
@@ -227,7 +231,7 @@ int gcache_cache_gather_upconvert_nvfp4_ds_mla(const void* src_cache, void* dst,
                                                int64_t num_blocks, int32_t block_size,
                                                int64_t block_stride, int64_t entry_stride,
                                                hipStream_t stream) {
-    return ds_gather(true, src_cache, dst, total_tokens, dst_stride, block_table, block_table_stride,
+    return ds_gather(kFmtNvfp4, src_cache, dst, total_tokens, dst_stride, block_table, block_table_stride,
                      workspace_starts, seq_starts, batch_size, num_blocks, block_size, block_stride,
                      entry_stride, stream);
 }
@@ -241,7 +245,18 @@ int gcache_cache_gather_upconvert_fp8_ds_mla(const void* src_cache, void* dst,
                                              int64_t num_blocks, int32_t block_size,
                                              int64_t block_stride, int64_t entry_stride,
                                              hipStream_t stream) {
-    return ds_gather(false, src_cache, dst, total_tokens, dst_stride, block_table, block_table_stride,
+    return ds_gather(kFmtFp8, src_cache, dst, total_tokens, dst_stride, block_table, block_table_stride,
+                     workspace_starts, seq_starts, batch_size, num_blocks, block_size, block_stride,
+                     entry_stride, stream);
+}
+
+int gcache_cache_gather_bf16(const void* src_cache, void* dst, int64_t total_tokens,
+                             int64_t dst_stride, const int32_t* block_table,
+                             int64_t block_table_stride, const int32_t* workspace_starts,
+                             const int32_t* seq_starts, int32_t batch_size, int64_t num_blocks,
+                             int32_t block_size, int64_t block_stride, int64_t entry_stride,
+                             hipStream_t stream) {
+    return ds_gather(kFmtBf16, src_cache, dst, total_tokens, dst_stride, block_table, block_table_stride,
                      workspace_starts, seq_starts, batch_size, num_blocks, block_size, block_stride,
                      entry_stride, stream);
 }

@@ -78,6 +78,7 @@ hipError_t launch_write_nvfp4_ds_mla(const DsMlaWriteParams& p, hipStream_t s);
 hipError_t launch_write_fp8_ds_mla(const DsMlaWriteParams& p, hipStream_t s);
 hipError_t launch_gather_nvfp4_ds_mla(const DsMlaGatherParams& p, hipStream_t s);
 hipError_t launch_gather_fp8_ds_mla(const DsMlaGatherParams& p, hipStream_t s);
+hipError_t launch_gather_bf16(const DsMlaGatherParams& p, hipStream_t s);
 hipError_t launch_reshape_and_cache_nvfp4(const KvWriteParams& p, hipStream_t s);
 hipError_t launch_gather_nvfp4_kv(const KvGatherParams& p, hipStream_t s);
 

@@ -38,11 +38,11 @@ __global__ __launch_bounds__(kBlockThreads) void k_reshape_and_cache_nvfp4(KvWri
     const int64_t t = wave0 + (int64_t)blockIdx.x * kWavesPerBlock + wave_id();
     if (t >= p.num_tokens) return;
     {
-        const int64_t slot = valid_slot(p.slots[t], p.num_slots);
-        if (slot < 0) return;                             // padding token (wave-uniform)
-        int64_t blk, off;
-        split_block(slot, p.div, blk, off);
+        // The slot, the scales and the first pass of inputs are loaded
+        // together (a skipped token's inputs are read but never used).
+        const int64_t slot_in = p.slots[t];
         const float gs_k = *p.gscale[0], gs_v = *p.gscale[1];
+        int64_t slot = -1, blk = 0, off = 0;
 
         for (int base = 0; base < nitems; base += kKvItemsPerLane * kWave) {
             uint4 v0[kKvItemsPerLane], v1[kKvItemsPerLane];
@@ -58,6 +58,11 @@ __global__ __launch_bounds__(kBlockThreads) void k_reshape_and_cache_nvfp4(KvWri
                     v0[u] = ld_stream16(src);
                     v1[u] = ld_stream16(src + 16);
                 }
+            }
+            if (base == 0) {
+                slot = valid_slot(slot_in, p.num_slots);
+                if (slot < 0) return;                     // skipped token (wave-uniform)
+                split_block(slot, p.div, blk, off);
             }
 #pragma unroll
             for (int u = 0; u < kKvItemsPerLane; u++) {
@@ -112,10 +117,25 @@ __global__ __launch_bounds__(kBlockThreads) void k_gather_nvfp4_kv(KvGatherParam
     const int nitems = 2 * nchunk;                       // both sides
     const int64_t r = wave0 + (int64_t)blockIdx.x * kWavesPerBlock + wave_id();
     if (r >= p.total) return;
-    // wave-uniform walk of row r; blk < 0: the walk leaves the block table
-    // or the cache, and the row is written as zeros
-    const int b = find_request(p.ws, p.batch, r, p.total);
-    const int64_t pos = (p.seq_starts ? (int64_t)p.seq_starts[b] : 0) + (r - (int64_t)p.ws[b]);
+    // Wave-uniform walk of row r.  The interpolated guess g and its
+    // neighbour are loaded together with seq_starts[g]: when
+    // ws[g] <= r < ws[g+1] the request is g and no further load is needed
+    // (one request per row, or evenly sized requests); otherwise the full
+    // search runs.  blk < 0: the walk leaves the block table or the cache,
+    // and the row is written as zeros.
+    int g = (int)((r * (int64_t)p.batch) / p.total);
+    if (g >= p.batch) g = p.batch - 1;
+    const int64_t ws_g = p.ws[g];
+    const int64_t ws_n = g + 1 < p.batch ? (int64_t)p.ws[g + 1] : INT64_MAX;
+    const int64_t ss_g = p.seq_starts ? (int64_t)p.seq_starts[g] : 0;
+    int b = g;
+    int64_t ws_b = ws_g, ss_b = ss_g;
+    if (!(ws_g <= r && r < ws_n)) {
+        b = find_request(p.ws, p.batch, r, p.total);
+        ws_b = p.ws[b];
+        ss_b = p.seq_starts ? (int64_t)p.seq_starts[b] : 0;
+    }
+    const int64_t pos = ss_b + (r - ws_b);
     int64_t bi = -1, off = 0, blk = -1;
     if (pos >= 0) split_block(pos, p.div, bi, off);
     if (bi >= 0 && bi < p.bt_stride) {

@@ -190,6 +190,24 @@ int gcache_cache_gather_upconvert_fp8_ds_mla(const void* src_cache, void* dst,
                                              hipStream_t stream);
 
 /*
+ * BF16 comparator gather -- the unquantized MLA cache that the two formats
+ * above replace ([PR48642] "Key source excerpts": _compute_prefill_context
+ * keeps the original bf16 gather for caches that are not fp8_ds_mla).  Same
+ * walk, arguments and zero rows as the DS-MLA gathers; each entry is the
+ * row's 576 bf16 values (1152 bytes, NoPE then RoPE) and is copied to
+ *     dst[r, 0:576] unchanged.
+ * It bounds what a walk-driven gather can reach on the device: the
+ * quantized gathers read 352 or 656 bytes per row where this one reads
+ * 1152.  Requirements as for the nvfp4 gather with entry_stride >= 1152.
+ */
+int gcache_cache_gather_bf16(const void* src_cache, void* dst, int64_t total_tokens,
+                             int64_t dst_stride, const int32_t* block_table,
+                             int64_t block_table_stride, const int32_t* workspace_starts,
+                             const int32_t* seq_starts, int32_t batch_size, int64_t num_blocks,
+                             int32_t block_size, int64_t block_stride, int64_t entry_stride,
+                             hipStream_t stream);
+
+/*
  * Per-head NVFP4 K/V cache geometry, in BYTES from the start of the cache
  * ([PR37332] "Key source excerpts": allocation (num_blocks, 2, block_size,
  * num_heads, full_dim), split views into data and scale parts that keep the
@@ -219,7 +237,8 @@ int gcache_nvfp4_kv_split_layout(int32_t block_size, int32_t num_heads, int32_t 
  * "Implementation breakdown" item 4.
  *
  * For every token t with 0 <= slot < num_blocks * block_size (other slot
- * ids are skipped, -1 being padding; block slot / block_size, offset
+ * ids are skipped, -1 being padding: their cache bytes are never written,
+ * though their key/value rows may be read; block slot / block_size, offset
  * slot % block_size), side c in {K, V} with per-tensor scale gs (*k_scale or
  * *v_scale, device fp32 scalars > 0), head h and 16-value block j:
  *     sf = e4m3_rn_sat((amax / 6) / gs);  e = dec(sf) * gs;

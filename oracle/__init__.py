@@ -60,6 +60,8 @@ def lib():
                                         _I64, _I64],
             "orc_gather_fp8_ds_mla": [_P, _I64, _P, _I64, _I64, _P, _I64, _P, _P, _I32, _I64, _I32,
                                       _I64, _I64],
+            "orc_gather_bf16": [_P, _I64, _P, _I64, _I64, _P, _I64, _P, _P, _I32, _I64, _I32,
+                                _I64, _I64],
             "orc_gather_walk": [_I64, _P, _I64, _P, _P, _I32, _I64, _I32, _P, _P],
             "orc_kv_layout_split": [_I32, _I32, _I32, C.POINTER(KvLayout)],
             "orc_reshape_and_cache_nvfp4": [_P, _P, _I64, _I64, _I64, _I64, _P, _I64, _P, _I64, _I32,
@@ -221,6 +223,16 @@ def gather_fp8_ds_mla(cache, total_tokens, block_table, workspace_starts, seq_st
     if block_stride is None:
         block_stride = block_size * entry_stride
     return _gather(lib().orc_gather_fp8_ds_mla, "gather_fp8_ds_mla", cache, total_tokens,
+                   block_table, workspace_starts, seq_starts, num_blocks, block_size,
+                   block_stride, entry_stride, dst)
+
+
+def gather_bf16(cache, total_tokens, block_table, workspace_starts, seq_starts,
+                num_blocks, block_size, block_stride=None, entry_stride=1152, dst=None):
+    """BF16 comparator: the same walk over 1152-byte bf16 entries, copied."""
+    if block_stride is None:
+        block_stride = block_size * entry_stride
+    return _gather(lib().orc_gather_bf16, "gather_bf16", cache, total_tokens,
                    block_table, workspace_starts, seq_starts, num_blocks, block_size,
                    block_stride, entry_stride, dst)
 

@@ -487,6 +487,29 @@ int orc_gather_fp8_ds_mla(const uint8_t* cache, int64_t cache_bytes,
                          decode_fp8_row);
 }
 
+/* BF16 comparator (the plain bf16 MLA cache that the quantized formats
+ * replace; vLLM PR #48642 digest, the _compute_prefill_context excerpt,
+ * keeps it as the path for unquantized caches): the same walk, each
+ * 1152-byte entry holds the row's 576 bf16 values (NoPE then RoPE, little
+ * endian) and is copied unchanged. */
+static void copy_bf16_row(const uint8_t* entry, uint16_t* row) {
+    for (int i = 0; i < ROW_DIM; i++)
+        row[i] = (uint16_t)(entry[2 * i] | (entry[2 * i + 1] << 8));
+}
+
+int orc_gather_bf16(const uint8_t* cache, int64_t cache_bytes,
+                    uint16_t* dst, int64_t total_tokens, int64_t dst_stride,
+                    const int32_t* block_table, int64_t block_table_stride,
+                    const int32_t* workspace_starts, const int32_t* seq_starts,
+                    int32_t batch_size, int64_t num_blocks, int32_t block_size,
+                    int64_t block_stride, int64_t entry_stride) {
+    return gather_ds_mla(cache, cache_bytes, dst, total_tokens, dst_stride, block_table,
+                         block_table_stride, workspace_starts, seq_starts, batch_size,
+                         num_blocks, block_size, block_stride, entry_stride, 2 * ROW_DIM,
+                         copy_bf16_row);
+}
+
+
 /* ------------------------------------------------------------------------ */
 /* O5 / O6: per-head NVFP4 K/V cache.                                        */
 /* vLLM PR #37332 digest: "Motivation" and "Implementation breakdown" item 4 */

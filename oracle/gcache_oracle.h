@@ -108,6 +108,15 @@ int orc_gather_fp8_ds_mla(const uint8_t* cache, int64_t cache_bytes,
                           int32_t batch_size, int64_t num_blocks, int32_t block_size,
                           int64_t block_stride, int64_t entry_stride);
 
+/* BF16 comparator: the same walk over a cache of 1152-byte entries holding
+ * the row's 576 bf16 values; rows are copied unchanged. */
+int orc_gather_bf16(const uint8_t* cache, int64_t cache_bytes,
+                    uint16_t* dst, int64_t total_tokens, int64_t dst_stride,
+                    const int32_t* block_table, int64_t block_table_stride,
+                    const int32_t* workspace_starts, const int32_t* seq_starts,
+                    int32_t batch_size, int64_t num_blocks, int32_t block_size,
+                    int64_t block_stride, int64_t entry_stride);
+
 /* Walk only: for each workspace row, the (block id, offset in block) that
  * the gather reads.  out_block / out_offset have total_tokens entries. */
 int orc_gather_walk(int64_t total_tokens,

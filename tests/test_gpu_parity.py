@@ -247,6 +247,58 @@ def test_out_of_range_metadata(g, orc, fmt):
     assert_same(host(dst), exp, f"{fmt} gather with out-of-range metadata")
 
 
+def _bf16_gather_case(orc, g, cache_bits, gcase, nb, bs, estr_el, bt=None, zero_rows=None):
+    """GPU BF16 comparator gather vs the oracle on bf16 cache bits
+    [nb, bs, estr_el] (rows with an invalid walk expected as zeros)."""
+    bt = gcase.block_table if bt is None else bt
+    flat = cache_bits.reshape(-1).view(np.uint8)
+    if zero_rows is None:
+        want = orc.gather_bf16(flat, gcase.total_tokens, bt, gcase.workspace_starts, gcase.seq_starts, nb,
+                               bs, bs * estr_el * 2, estr_el * 2)
+    else:
+        want = zero_rows
+    cache_dev = dev(cache_bits)[:, :, :576] if estr_el > 576 else dev(cache_bits)
+    dst = dev(np.full((gcase.total_tokens, 576), 0x7FC1, np.uint16))
+    g.cache_gather_bf16(cache_dev, dst, dev(bt), dev(gcase.workspace_starts), dev(gcase.seq_starts))
+    torch.cuda.synchronize()
+    assert_same(host(dst), want, f"bf16 gather ({gcase.name})")
+
+
+def test_bf16_comparator_gather(g, orc):
+    """The BF16 comparator copies the walked rows bit for bit (random bits,
+    NaN patterns included): prefill-like requests, 65 requests (memory
+    search), padded entries, and zero rows for an invalid walk."""
+    rng = np.random.default_rng(55)
+    nb, bs = 80, 16
+    for estr_el in (576, 600):
+        cache = rng.integers(0, 1 << 16, size=(nb, bs, estr_el), dtype=np.uint16)
+        for B in (3, 65):
+            gc_ = synth.prefill_gather(rng, f"bf16-B{B}", B, 0, 9, nb, bs, 1)
+            _bf16_gather_case(orc, g, cache, gc_, nb, bs, estr_el)
+        gc_ = synth.prefill_gather(rng, "bf16-long", 4, 20, 150, nb, bs, 10)
+        _bf16_gather_case(orc, g, cache, gc_, nb, bs, estr_el)
+    # invalid walk: expected rows from a per-row oracle gather, zeros elsewhere
+    cache = rng.integers(0, 1 << 16, size=(6, 16, 576), dtype=np.uint16)
+    bt, ws, ss, total = _bad_metadata(6, 16)
+    rs = _walk_slots(total, bt, ws, ss, 16, 6)
+    ok = rs >= 0
+    pt = synth.per_token_gather("valid rows", rs[ok], 6, 16)
+    exp = np.zeros((total, 576), np.uint16)
+    exp[ok] = orc.gather_bf16(cache.reshape(-1).view(np.uint8), pt.total_tokens, pt.block_table,
+                              pt.workspace_starts, pt.seq_starts, 6, 16)
+    gc_ = synth.GatherCase("bf16-bad-metadata", bt, ws, ss, total, 6, 16, None)
+    _bf16_gather_case(orc, g, cache, gc_, 6, 16, 576, zero_rows=exp)
+
+
+def test_bf16_comparator_gather_full_size(g, orc):
+    """The nvfp4 prefill gather's requests over a bf16 cache of the same
+    geometry (8192 blocks x 64 x 1152 B): every row compared."""
+    gcase = synth.config3_gather()
+    cache = synth.normal_bf16_rows(1013, 0, gcase.num_blocks * gcase.block_size, 576)
+    _bf16_gather_case(orc, g, cache.reshape(gcase.num_blocks, gcase.block_size, 576), gcase,
+                      gcase.num_blocks, gcase.block_size, 576)
+
+
 # ---------------------------------------------------------------------------
 # per-head NVFP4 K/V
 # ---------------------------------------------------------------------------

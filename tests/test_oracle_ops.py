@@ -314,6 +314,24 @@ def test_address_tags_pin_the_walk(orc):
     assert np.array_equal(got, blk * bs + off)
 
 
+def test_bf16_comparator_gather_vs_brute_force(orc):
+    """The BF16 comparator copies the 1152 entry bytes of the row that a
+    linear-scan walk names, as 576 little-endian bf16 values: random cache
+    bytes, padded entries, gaps between blocks, empty requests."""
+    rng = np.random.default_rng(33)
+    nb, bs = 12, 16
+    estr = 1152 + 64
+    bstr = bs * estr + 128
+    cache = rng.integers(0, 256, size=nb * bstr, dtype=np.uint8)
+    g = synth.prefill_gather(rng, "bf16", 5, 0, 40, nb, bs, 3)
+    d = orc.gather_bf16(cache, g.total_tokens, g.block_table, g.workspace_starts, g.seq_starts, nb, bs,
+                        bstr, estr)
+    blk, off = brute.walk(g.total_tokens, g.block_table, g.workspace_starts, g.seq_starts, bs)
+    want = np.stack([cache[b * bstr + o * estr: b * bstr + o * estr + 1152].view("<u2")
+                     for b, o in zip(blk, off)]) if g.total_tokens else np.zeros((0, 576), np.uint16)
+    assert np.array_equal(d, want)
+
+
 def test_padding_and_untouched_bytes_keep_sentinels(orc):
     w = synth.config2()
     for fill in (0xA5, 0x5A):
