@@ -195,7 +195,7 @@ def main():
                          "GB_per_s": round(nbytes / (ms * 1e6), 1),
                          "frac_of_hbm_peak": round(nbytes / (ms * 1e6) / HBM_PEAK_GBS, 4)}
 
-    extras = None if args.no_extras else measure_extras(torch, gc, g3, args.steps, dev_arr)
+    extras = None if args.no_extras else measure_extras(torch, gc, g3, args.steps, dev_arr, d["cache3"])
 
     if args.copy_calibration:
         # a plain elementwise kernel that reads and writes exactly n bytes each
@@ -244,11 +244,14 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def measure_extras(torch, gc, g3, steps, dev_arr):
-    """Outside the timed step: the BF16 comparator gather (same walk, 1152-byte
-    bf16 entries copied) over the nvfp4 prefill gather's requests and cache
-    geometry -- what a walk-driven gather of full rows reaches on this device.
-    HIP events around each launch on the launch stream, mean over `steps`."""
+def measure_extras(torch, gc, g3, steps, dev_arr, cache3):
+    """Outside the timed step: (1) the BF16 comparator gather (same walk,
+    1152-byte bf16 entries copied) over the nvfp4 prefill gather's requests
+    and cache geometry -- what a walk-driven gather of full rows reaches on
+    this device; (2) the chunked-context driver gathering every request's
+    whole nvfp4 context (lengths of the prefill gather's requests, from
+    position 0) through a 65536-row workspace.  HIP events on the launch
+    stream, mean over `steps`."""
     import synth
     nb, bs = g3.num_blocks, g3.block_size
     cache = torch.from_numpy(synth.normal_bf16_rows(1013, 0, nb * bs, 576).view(np.int16)) \
@@ -267,12 +270,55 @@ def measure_extras(torch, gc, g3, steps, dev_arr):
     ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
     nbytes = g3.total_tokens * 2 * 1152
     del cache, dst
-    return {"bf16_gather_comparator": {
+    out = {"bf16_gather_comparator": {
         "ms": round(ms, 5), "bytes": nbytes, "units": g3.total_tokens,
         "GB_per_s": round(nbytes / (ms * 1e6), 1), "frac_of_hbm_peak": round(nbytes / (ms * 1e6) / HBM_PEAK_GBS, 4),
         "rows_per_s": round(g3.total_tokens / (ms * 1e-3), 1),
         "workload": f"{g3.total_tokens} rows of the nvfp4 prefill gather over a bf16 cache "
                     f"{nb} x {bs} x 1152 B (1152 B read + 1152 B written per row)"}}
+
+    lens = np.asarray(g3.lengths, np.int32)
+    ws_rows = 65536
+    workspace = torch.empty((ws_rows, 576), dtype=torch.bfloat16, device="cuda")
+    _, plan = gc.context_chunks(lens, ws_rows, bs)
+    rows = int(sum(t for _, _, t in plan))
+
+    # Device time: the chunk gathers are enqueued behind a short spin kernel,
+    # so they run back to back and the events around them see only GPU work
+    # (metadata upload included).  Wall time: the same pass enqueued on an
+    # idle GPU, so the host's per-chunk call overhead shows as gaps.
+    def chunked():
+        for _ in gc.gather_context_chunked(gc.cache_gather_upconvert_nvfp4_ds_mla, cache3, workspace, bt, lens):
+            pass
+    chunked()
+    mk = lambda: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    dev_t, wall_t = [], []
+    for i in range(steps):
+        a, b = mk()
+        torch.cuda._sleep(2_000_000)
+        a.record()
+        chunked()
+        b.record()
+        torch.cuda.synchronize()
+        dev_t.append(a.elapsed_time(b))
+        a, b = mk()
+        a.record()
+        chunked()
+        b.record()
+        torch.cuda.synchronize()
+        wall_t.append(a.elapsed_time(b))
+    busy, wall = float(np.mean(dev_t)), float(np.mean(wall_t))
+    nbytes = rows * (NV + 1152)
+    out["chunked_context_nvfp4_gather"] = {
+        "ms": round(busy, 5), "wall_ms": round(wall, 5), "bytes": nbytes, "units": rows, "chunks": len(plan),
+        "GB_per_s": round(nbytes / (busy * 1e6), 1), "frac_of_hbm_peak": round(nbytes / (busy * 1e6) / HBM_PEAK_GBS, 4),
+        "wall_GB_per_s": round(nbytes / (wall * 1e6), 1),
+        "workload": f"whole contexts of the {lens.shape[0]} prefill requests ({rows} positions) gathered in "
+                    f"{len(plan)} chunks through a {ws_rows}-row workspace; ms = device time of the pass "
+                    "(launches queued behind a spin kernel), wall_ms = the pass on an idle GPU, host call "
+                    "overhead included"}
+    del workspace
+    return out
 
 
 def measure_cold(torch, ops, reps=5):

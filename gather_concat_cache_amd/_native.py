@@ -9,6 +9,7 @@ importing this module fails when the library has not been built.
 import ctypes as C
 import os
 
+import numpy as np
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -49,6 +50,8 @@ _SIGS = {
     "gcache_cache_gather_bf16": (C.c_int, [_P, _P, _I64, _I64, _P, _I64, _P, _P, _I32, _I64, _I32, _I64,
                                            _I64, _P]),
     "gcache_nvfp4_kv_split_layout": (C.c_int, [_I32, _I32, _I32, C.POINTER(NvFp4KvLayout)]),
+    "gcache_context_chunk_plan": (C.c_int, [_P, _I32, _I64, _I32, _P, _P]),
+    "gcache_context_chunk": (C.c_int, [_P, _I32, _I32, _I32, _P, _P, _P]),
     "gcache_reshape_and_cache_nvfp4": (C.c_int, [_P, _P, _I64, _I64, _I64, _I64, _P, _P, _I64, _I32, _I32, _I64,
                                                  _I32, C.POINTER(NvFp4KvLayout), _P, _P, _P]),
     "gcache_gather_upconvert_nvfp4_kv": (C.c_int, [_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P, _I64, _P, _P,
@@ -65,7 +68,7 @@ def load():
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"{LIB_PATH} is missing: build it with "
-                              "`python -m gather_concat_cache_amd.build` (hipcc, gfx950)")
+                              "`python gather_concat_cache_amd/build.py` (hipcc, gfx950)")
         lib = C.CDLL(LIB_PATH)
         for name, (res, args) in _SIGS.items():
             fn = getattr(lib, name)
@@ -289,3 +292,51 @@ def gather_upconvert_nvfp4_kv(kv_cache, key_out, value_out, block_table, workspa
             _ptr(workspace_starts), _ptr(seq_starts), B, H, hs, nb, bs, C.byref(layout),
             _ptr(k_scale), _ptr(v_scale), _stream(dev, stream))
     _check(st, "gather_upconvert_nvfp4_kv")
+
+
+# ---------------------------------------------------------------------------
+# chunked context (host plan from the library, gathers on the device)
+# ---------------------------------------------------------------------------
+def context_chunks(context_lens, workspace_rows, block_size):
+    """Host plan of a chunked-context gather: (chunk_rows, [(seq_starts,
+    workspace_starts, total_rows), ...]) as int32 NumPy arrays."""
+    lens = np.ascontiguousarray(np.asarray(context_lens, dtype=np.int32))
+    B = lens.shape[0]
+    lib = load()
+    c, n = C.c_int32(), C.c_int32()
+    _check(lib.gcache_context_chunk_plan(lens.ctypes.data, B, int(workspace_rows), int(block_size),
+                                         C.addressof(c), C.addressof(n)), "gcache_context_chunk_plan")
+    chunks = []
+    for i in range(n.value):
+        ss = np.empty(B, np.int32)
+        ws = np.empty(B, np.int32)
+        tot = C.c_int64()
+        _check(lib.gcache_context_chunk(lens.ctypes.data, B, c.value, i, ss.ctypes.data, ws.ctypes.data,
+                                        C.addressof(tot)), "gcache_context_chunk")
+        chunks.append((ss, ws, tot.value))
+    return c.value, chunks
+
+
+def gather_context_chunked(gather, src_cache, workspace, block_table, context_lens, stream=None):
+    """Gather every request's whole cached context (positions 0 ..
+    context_lens[b]-1) through a bounded bf16 workspace [rows, >=576], one
+    chunk at a time.  `gather` is one of cache_gather_upconvert_nvfp4_ds_mla,
+    cache_gather_upconvert_fp8_ds_mla or cache_gather_bf16.  Yields
+    (chunk index, workspace[:total_rows]) after enqueuing each chunk's gather
+    on the stream; consume (or copy) a chunk before asking for the next one,
+    which overwrites the workspace.  All chunks' metadata is uploaded once."""
+    lens = np.asarray(context_lens, dtype=np.int32)
+    block_size = src_cache.shape[1]
+    _, chunks = context_chunks(lens, workspace.shape[0], block_size)
+    if not chunks:
+        return
+    # one upload of every chunk's metadata [chunks, 2, B] from pinned host
+    # memory, ordered on the stream before the first gather
+    host_meta = torch.from_numpy(np.stack([np.stack([ss, ws]) for ss, ws, _ in chunks])).pin_memory()
+    s = torch.cuda.current_stream(workspace.device) if stream is None else stream
+    with torch.cuda.stream(s):
+        meta = host_meta.to(workspace.device, non_blocking=True)
+    for i, (_, _, total) in enumerate(chunks):
+        rows = workspace[:total]
+        gather(src_cache, rows, block_table, meta[i, 1], meta[i, 0], stream=stream)
+        yield i, rows

@@ -250,6 +250,50 @@ int gcache_cache_gather_upconvert_fp8_ds_mla(const void* src_cache, void* dst,
                      entry_stride, stream);
 }
 
+int gcache_context_chunk_plan(const int32_t* context_lens, int32_t batch_size,
+                              int64_t workspace_rows, int32_t block_size,
+                              int32_t* chunk_rows, int32_t* num_chunks) {
+    if (!context_lens || !chunk_rows || !num_chunks) return GCACHE_ERR_NULL;
+    if (batch_size <= 0 || block_size <= 0 || workspace_rows < 0) return GCACHE_ERR_SHAPE;
+    int32_t longest = 0;
+    for (int32_t b = 0; b < batch_size; b++) {
+        if (context_lens[b] < 0) return GCACHE_ERR_SHAPE;
+        longest = context_lens[b] > longest ? context_lens[b] : longest;
+    }
+    // a chunk's rows are addressed with int32 workspace_starts
+    const int64_t usable = workspace_rows < INT32_MAX ? workspace_rows : INT32_MAX;
+    const int64_t c = usable / batch_size / block_size * block_size;
+    if (c <= 0) return GCACHE_ERR_SHAPE;                    // not one block per request
+    *chunk_rows = (int32_t)c;
+    *num_chunks = (int32_t)((longest + c - 1) / c);
+    return GCACHE_OK;
+}
+
+int gcache_context_chunk(const int32_t* context_lens, int32_t batch_size, int32_t chunk_rows,
+                         int32_t chunk, int32_t* seq_starts, int32_t* workspace_starts,
+                         int64_t* total_rows) {
+    if (!context_lens || !seq_starts || !workspace_starts || !total_rows) return GCACHE_ERR_NULL;
+    if (batch_size <= 0 || chunk_rows <= 0 || chunk < 0) return GCACHE_ERR_SHAPE;
+    const int64_t start = (int64_t)chunk * chunk_rows;
+    int64_t total = 0;
+    bool any = false;
+    for (int32_t b = 0; b < batch_size; b++) {
+        if (context_lens[b] < 0) return GCACHE_ERR_SHAPE;
+        any = any || context_lens[b] > start;
+    }
+    if (!any || start > INT32_MAX) return GCACHE_ERR_SHAPE;  // chunk past the longest context
+    for (int32_t b = 0; b < batch_size; b++) {
+        int64_t len = context_lens[b] - start;
+        len = len < 0 ? 0 : (len > chunk_rows ? chunk_rows : len);
+        if (total > INT32_MAX) return GCACHE_ERR_SHAPE;
+        seq_starts[b] = (int32_t)start;
+        workspace_starts[b] = (int32_t)total;
+        total += len;
+    }
+    *total_rows = total;
+    return GCACHE_OK;
+}
+
 int gcache_cache_gather_bf16(const void* src_cache, void* dst, int64_t total_tokens,
                              int64_t dst_stride, const int32_t* block_table,
                              int64_t block_table_stride, const int32_t* workspace_starts,

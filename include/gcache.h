@@ -30,10 +30,13 @@
  *    rejected (nothing is launched then), when the current device is not a
  *    gfx950 GPU (GCACHE_ERR_UNSUPPORTED) or when the launch itself fails.
  *    Faults inside a kernel surface at the caller's next synchronization.
- *  - Not checked (caller contract, as in the pages' kernels): slot and block
- *    ids lie inside the cache, slots are distinct, workspace_starts is
- *    non-decreasing with workspace_starts[0] == 0, and every block-table entry
- *    a row reads is valid.  Inputs are finite.
+ *  - Checked inside the kernels: slot ids outside the cache are skipped like
+ *    padding, and gather rows whose walk leaves the block-table row or names
+ *    a block outside the cache are written as zeros, so no metadata value
+ *    makes a kernel touch memory outside its arguments.
+ *  - Not checked (caller contract, as in the pages' kernels): slots are
+ *    distinct, workspace_starts is non-decreasing with workspace_starts[0]
+ *    == 0 (otherwise rows map to unspecified requests), inputs are finite.
  *  - Calls are asynchronous and stream-ordered; two calls that write the same
  *    cache bytes on different streams race.
  *
@@ -206,6 +209,37 @@ int gcache_cache_gather_bf16(const void* src_cache, void* dst, int64_t total_tok
                              const int32_t* seq_starts, int32_t batch_size, int64_t num_blocks,
                              int32_t block_size, int64_t block_stride, int64_t entry_stride,
                              hipStream_t stream);
+
+/*
+ * Chunked-context plan -- [PR48642] "Key source excerpts"
+ * (_compute_prefill_context): a prefill whose cached context does not fit
+ * the bf16 workspace gathers it in chunks; chunk i runs the gather with
+ * workspace_starts = cu_seq_lens[i], seq_starts = starts[i] into the first
+ * seq_tot[i] workspace rows.  HOST functions: every pointer is host memory,
+ * nothing touches the device.
+ *
+ * gcache_context_chunk_plan: chunk_rows = the largest multiple of block_size
+ * with batch_size * chunk_rows <= workspace_rows; num_chunks =
+ * ceil(max context length / chunk_rows) (0 when every context is empty).
+ * gcache_context_chunk: for chunk index `chunk`, request b gets
+ *     seq_starts[b]       = chunk * chunk_rows
+ *     len_b               = clamp(context_lens[b] - chunk * chunk_rows, 0, chunk_rows)
+ *     workspace_starts[b] = len_0 + ... + len_{b-1},   *total_rows = sum of len_b
+ * so every context position of every request is gathered exactly once, in
+ * order, and no chunk needs more than workspace_rows rows.
+ *  context_lens     int32 [batch_size], >= 0
+ *  seq_starts, workspace_starts  int32 [batch_size] outputs
+ * Errors: GCACHE_ERR_NULL for a null pointer; GCACHE_ERR_SHAPE when
+ * batch_size <= 0, block_size <= 0, a context length is negative,
+ * workspace_rows < batch_size * block_size, or chunk is outside
+ * [0, num_chunks).
+ */
+int gcache_context_chunk_plan(const int32_t* context_lens, int32_t batch_size,
+                              int64_t workspace_rows, int32_t block_size,
+                              int32_t* chunk_rows, int32_t* num_chunks);
+int gcache_context_chunk(const int32_t* context_lens, int32_t batch_size, int32_t chunk_rows,
+                         int32_t chunk, int32_t* seq_starts, int32_t* workspace_starts,
+                         int64_t* total_rows);
 
 /*
  * Per-head NVFP4 K/V cache geometry, in BYTES from the start of the cache

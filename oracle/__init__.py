@@ -63,6 +63,8 @@ def lib():
             "orc_gather_bf16": [_P, _I64, _P, _I64, _I64, _P, _I64, _P, _P, _I32, _I64, _I32,
                                 _I64, _I64],
             "orc_gather_walk": [_I64, _P, _I64, _P, _P, _I32, _I64, _I32, _P, _P],
+            "orc_context_chunk_plan": [_P, _I32, _I64, _I32, _P, _P],
+            "orc_context_chunk": [_P, _I32, _I32, _I32, _P, _P, _P],
             "orc_kv_layout_split": [_I32, _I32, _I32, C.POINTER(KvLayout)],
             "orc_reshape_and_cache_nvfp4": [_P, _P, _I64, _I64, _I64, _I64, _P, _I64, _P, _I64, _I32,
                                             _I32, _I64, _I32, C.POINTER(KvLayout), _F32, _F32],
@@ -289,3 +291,22 @@ def gather_upconvert_nvfp4_kv(cache, total_tokens, block_table, workspace_starts
         head_size, num_blocks, block_size, C.byref(layout), float(k_scale), float(v_scale)),
         "gather_upconvert_nvfp4_kv")
     return k, v
+
+
+def context_chunks(context_lens, workspace_rows, block_size):
+    """Chunked-context plan: (chunk_rows, [(seq_starts, workspace_starts,
+    total_rows) for each chunk]) -- every context position gathered once."""
+    lens = _need(np.asarray(context_lens, np.int32), np.int32, "context_lens")
+    B = lens.shape[0]
+    c, n = C.c_int32(), C.c_int32()
+    _check(lib().orc_context_chunk_plan(_ptr(lens), B, int(workspace_rows), int(block_size),
+                                        C.byref(c), C.byref(n)), "context_chunk_plan")
+    out = []
+    for i in range(n.value):
+        ss = np.zeros(B, np.int32)
+        ws = np.zeros(B, np.int32)
+        tot = C.c_int64()
+        _check(lib().orc_context_chunk(_ptr(lens), B, c.value, i, _ptr(ss), _ptr(ws), C.byref(tot)),
+               "context_chunk")
+        out.append((ss, ws, tot.value))
+    return c.value, out

@@ -687,3 +687,47 @@ int orc_gather_upconvert_nvfp4_kv(const uint8_t* cache, int64_t cache_bytes,
     }
     return ORC_OK;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Chunked context (vLLM PR #48642 digest, the _compute_prefill_context      */
+/* excerpt): chunk i gathers, for every request, the context positions that  */
+/* fall in chunk i, into workspace rows laid out request after request.      */
+/* READING: chunk_rows is the largest multiple of block_size such that       */
+/* batch_size * chunk_rows <= workspace_rows (at most INT32_MAX); position p */
+/* of a request belongs to chunk p / chunk_rows; chunk i starts every        */
+/* request at position i * chunk_rows.                                       */
+/* ------------------------------------------------------------------------ */
+int orc_context_chunk_plan(const int32_t* context_lens, int32_t batch_size,
+                           int64_t workspace_rows, int32_t block_size,
+                           int32_t* chunk_rows, int32_t* num_chunks) {
+    if (!context_lens || batch_size <= 0 || block_size <= 0 || workspace_rows < 0)
+        return ORC_ERR_ARG;
+    int64_t limit = workspace_rows < INT32_MAX ? workspace_rows : INT32_MAX;
+    int64_t c = 0;                                  /* grow one block at a time */
+    while ((c + block_size) * (int64_t)batch_size <= limit) c += block_size;
+    if (c == 0) return ORC_ERR_ARG;
+    int32_t chunks = 0;
+    for (int32_t b = 0; b < batch_size; b++) {
+        if (context_lens[b] < 0) return ORC_ERR_ARG;
+        for (int64_t p = 0; p < context_lens[b]; p += c)   /* chunks this request touches */
+            if (p / c + 1 > chunks) chunks = (int32_t)(p / c + 1);
+    }
+    *chunk_rows = (int32_t)c;
+    *num_chunks = chunks;
+    return ORC_OK;
+}
+
+int orc_context_chunk(const int32_t* context_lens, int32_t batch_size, int32_t chunk_rows,
+                      int32_t chunk, int32_t* seq_starts, int32_t* workspace_starts,
+                      int64_t* total_rows) {
+    if (!context_lens || batch_size <= 0 || chunk_rows <= 0 || chunk < 0) return ORC_ERR_ARG;
+    int64_t rows = 0;
+    for (int32_t b = 0; b < batch_size; b++) {
+        workspace_starts[b] = (int32_t)rows;
+        seq_starts[b] = (int32_t)((int64_t)chunk * chunk_rows);
+        for (int64_t p = 0; p < context_lens[b]; p++)        /* count the chunk's positions */
+            if (p / chunk_rows == chunk) rows++;
+    }
+    *total_rows = rows;
+    return ORC_OK;
+}

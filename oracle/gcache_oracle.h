@@ -166,6 +166,17 @@ int orc_gather_upconvert_nvfp4_kv(const uint8_t* cache, int64_t cache_bytes,
                                   const orc_kv_layout* layout,
                                   float k_scale, float v_scale);
 
+/* ---- chunked context plan (host metadata of a chunked prefill) ------ */
+/* chunk_rows: largest multiple of block_size with batch_size * chunk_rows
+ * <= workspace_rows; position p of a request is gathered by chunk
+ * p / chunk_rows, whose rows hold requests one after another. */
+int orc_context_chunk_plan(const int32_t* context_lens, int32_t batch_size,
+                           int64_t workspace_rows, int32_t block_size,
+                           int32_t* chunk_rows, int32_t* num_chunks);
+int orc_context_chunk(const int32_t* context_lens, int32_t batch_size, int32_t chunk_rows,
+                      int32_t chunk, int32_t* seq_starts, int32_t* workspace_starts,
+                      int64_t* total_rows);
+
 #ifdef __cplusplus
 }
 #endif

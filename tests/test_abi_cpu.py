@@ -30,7 +30,13 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 11, names
+    assert names == sorted([
+        "gcache_entry_bytes", "gcache_nvfp4_full_dim", "gcache_status_string",
+        "gcache_cache_write_nvfp4_ds_mla", "gcache_cache_write_fp8_ds_mla",
+        "gcache_cache_gather_upconvert_nvfp4_ds_mla", "gcache_cache_gather_upconvert_fp8_ds_mla",
+        "gcache_cache_gather_bf16", "gcache_context_chunk_plan", "gcache_context_chunk",
+        "gcache_nvfp4_kv_split_layout", "gcache_reshape_and_cache_nvfp4",
+        "gcache_gather_upconvert_nvfp4_kv"]), names
     for n in names:
         assert hasattr(lib, n), f"{n} not exported by libgcache.so"
 

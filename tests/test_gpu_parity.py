@@ -299,6 +299,55 @@ def test_bf16_comparator_gather_full_size(g, orc):
                       gcase.num_blocks, gcase.block_size, 576)
 
 
+@pytest.mark.parametrize("fmt", ["nvfp4", "fp8", "bf16"])
+def test_chunked_context_gather(g, orc, fmt):
+    """Whole contexts gathered through a small workspace chunk by chunk equal
+    the oracle's one-shot gather of the same contexts, row for row
+    (contexts of 0, 1, one block, many blocks plus a tail; 9 chunks)."""
+    rng = np.random.default_rng(123)
+    nb, bs = 128, 16
+    lens = np.array([0, 1, 16, 700, 130, 1000, 64], np.int32)
+    B = lens.shape[0]
+    nblk = -(-lens // bs)
+    assert int(nblk.sum()) <= nb
+    perm = rng.permutation(nb).astype(np.int32)
+    bt = np.full((B, int(nblk.max())), -1, np.int32)
+    pos = 0
+    for b in range(B):
+        bt[b, :nblk[b]] = perm[pos:pos + nblk[b]]
+        pos += int(nblk[b])
+    full = synth.GatherCase("full", bt, np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int32),
+                            np.zeros(B, np.int32), int(lens.sum()), nb, bs, lens)
+    if fmt == "bf16":
+        cache_bits = rng.integers(0, 1 << 16, size=(nb, bs, 576), dtype=np.uint16)
+        cache_np = cache_bits.reshape(-1).view(np.uint8)
+        cache_dev = dev(cache_bits)
+        want = orc.gather_bf16(cache_np, full.total_tokens, bt, full.workspace_starts, full.seq_starts, nb, bs)
+        gather = g.cache_gather_bf16
+    else:
+        eb, _, gather = _ds_pair(fmt)
+        T = nb * bs
+        kv_c = synth.bf16_bits(rng.standard_normal((T, 512), dtype=np.float32))
+        k_pe = synth.bf16_bits(rng.standard_normal((T, 64), dtype=np.float32))
+        cache_np = np.zeros(T * eb, np.uint8)
+        owrite, ogather = _orc_ds(orc, fmt)
+        owrite(kv_c, k_pe, cache_np, np.arange(T, dtype=np.int64), nb, bs)
+        cache_dev = dev(cache_np).view(nb, bs, eb)
+        want = ogather(cache_np, full.total_tokens, bt, full.workspace_starts, full.seq_starts, nb, bs)
+    workspace = torch.zeros((7 * 48 + 5, 576), dtype=torch.bfloat16, device="cuda")
+    c, plan = g.context_chunks(lens, workspace.shape[0], bs)
+    assert c == 48 and len(plan) == 21
+    got = [[] for _ in range(B)]
+    for i, rows in g.gather_context_chunked(gather, cache_dev, workspace, dev(bt), lens):
+        h = host(rows)
+        ss, ws, tot = plan[i]
+        ends = np.concatenate([ws[1:], [tot]])
+        for b in range(B):
+            got[b].append(h[ws[b]:ends[b]])
+    got = np.concatenate([np.concatenate(x) if x else np.zeros((0, 576), np.uint16) for x in got])
+    assert_same(got, want, f"chunked {fmt} gather")
+
+
 # ---------------------------------------------------------------------------
 # per-head NVFP4 K/V
 # ---------------------------------------------------------------------------
