@@ -318,6 +318,27 @@ def measure_extras(torch, gc, g3, steps, dev_arr, cache3):
                     "(launches queued behind a spin kernel), wall_ms = the pass on an idle GPU, host call "
                     "overhead included"}
     del workspace
+
+    # (3) sparse index conversion: 4096 token rows x top-2048 positions
+    req, idx, sbt, sbs, snb = synth.sparse_index_case()
+    req_d, idx_d, sbt_d = dev_arr(req), dev_arr(idx), dev_arr(sbt)
+    sout = torch.empty_like(idx_d)
+    conv = lambda: gc.convert_req_index_to_global_index(req_d, idx_d, sbt_d, sbs, snb, out=sout)
+    for _ in range(3):
+        conv()
+    ev = [mk() for _ in range(steps)]
+    for a, b in ev:
+        a.record()
+        conv()
+        b.record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    nbytes = idx.size * 8 + req.size * 4
+    out["sparse_index_conversion"] = {
+        "ms": round(ms, 5), "bytes": nbytes, "units": int(idx.size),
+        "GB_per_s": round(nbytes / (ms * 1e6), 1), "frac_of_hbm_peak": round(nbytes / (ms * 1e6) / HBM_PEAK_GBS, 4),
+        "workload": f"{idx.shape[0]} token rows x top-{idx.shape[1]} positions over {sbt.shape[0]} requests "
+                    "(4 B read + 4 B written per index; block-table reads not counted)"}
     return out
 
 

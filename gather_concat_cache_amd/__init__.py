@@ -8,7 +8,8 @@ the ``gcache_`` prefix.
 """
 from ._native import (FP8_DS_MLA, LIB_PATH, NVFP4_DS_MLA, GcacheError, NvFp4KvLayout,
                       cache_gather_bf16, cache_gather_upconvert_fp8_ds_mla, cache_gather_upconvert_nvfp4_ds_mla,
-                      cache_write_fp8_ds_mla, cache_write_nvfp4_ds_mla, context_chunks, entry_bytes,
+                      cache_write_fp8_ds_mla, cache_write_nvfp4_ds_mla, context_chunks,
+                      convert_req_index_to_global_index, entry_bytes,
                       gather_context_chunked,
                       gather_upconvert_nvfp4_kv, load, nvfp4_full_dim, nvfp4_kv_split_layout,
                       reshape_and_cache_nvfp4)
@@ -19,7 +20,7 @@ __all__ = [
     "cache_write_nvfp4_ds_mla", "cache_write_fp8_ds_mla",
     "cache_gather_upconvert_nvfp4_ds_mla", "cache_gather_upconvert_fp8_ds_mla", "cache_gather_bf16",
     "reshape_and_cache_nvfp4", "gather_upconvert_nvfp4_kv",
-    "context_chunks", "gather_context_chunked",
+    "context_chunks", "gather_context_chunked", "convert_req_index_to_global_index",
 ]
 
 load()   # fail at import time when libgcache.so has not been built

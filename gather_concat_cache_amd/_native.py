@@ -51,6 +51,8 @@ _SIGS = {
                                            _I64, _P]),
     "gcache_nvfp4_kv_split_layout": (C.c_int, [_I32, _I32, _I32, C.POINTER(NvFp4KvLayout)]),
     "gcache_context_chunk_plan": (C.c_int, [_P, _I32, _I64, _I32, _P, _P]),
+    "gcache_convert_req_index_to_global_index": (C.c_int, [_P, _I64, _P, _I64, _I32, _I64, _P, _I32, _I64,
+                                                           _I32, _I64, _P, _I64, _P]),
     "gcache_context_chunk": (C.c_int, [_P, _I32, _I32, _I32, _P, _P, _P]),
     "gcache_reshape_and_cache_nvfp4": (C.c_int, [_P, _P, _I64, _I64, _I64, _I64, _P, _P, _I64, _I32, _I32, _I64,
                                                  _I32, C.POINTER(NvFp4KvLayout), _P, _P, _P]),
@@ -340,3 +342,38 @@ def gather_context_chunked(gather, src_cache, workspace, block_table, context_le
         rows = workspace[:total]
         gather(src_cache, rows, block_table, meta[i, 1], meta[i, 0], stream=stream)
         yield i, rows
+
+
+# ---------------------------------------------------------------------------
+# sparse index conversion
+# ---------------------------------------------------------------------------
+def convert_req_index_to_global_index(req_id, token_indices, block_table, block_size, num_blocks,
+                                      out=None, stream=None):
+    """Top-k positions local to each token's request -> global slot ids:
+    out[t, k] = block_table[req_id[t], i // block_size] * block_size + i % block_size
+    for i = token_indices[t, k], -1 where invalid.  req_id int32 [T] must have
+    exactly one entry per token row (the call is rejected otherwise);
+    token_indices int32 [T, topk]; block_table int32 [batch, max_blocks].
+    Returns out (int32 [T, topk], allocated when not given)."""
+    dev = _dev_tensor(token_indices, torch.int32, "token_indices").device
+    _dev_tensor(req_id, torch.int32, "req_id", dev)
+    _dev_tensor(block_table, torch.int32, "block_table", dev)
+    if token_indices.dim() != 2 or token_indices.stride(1) != 1:
+        raise ValueError("token_indices must be int32 [num_tokens, topk] with unit last stride")
+    if block_table.dim() != 2 or block_table.stride(1) != 1:
+        raise ValueError("block_table must be int32 [batch, max_blocks] with unit last stride")
+    if req_id.dim() != 1 or req_id.stride(0) != 1:
+        raise ValueError("req_id must be a contiguous int32 vector")
+    T, K = token_indices.shape
+    if out is None:
+        out = torch.empty((T, K), dtype=torch.int32, device=dev)
+    _dev_tensor(out, torch.int32, "out", dev)
+    if out.dim() != 2 or out.shape[0] != T or out.shape[1] < K or out.stride(1) != 1:
+        raise ValueError("out must be int32 [num_tokens, >=topk] with unit last stride")
+    with torch.cuda.device(dev):
+        st = load().gcache_convert_req_index_to_global_index(
+            _ptr(req_id), req_id.shape[0], _ptr(token_indices), T, K, token_indices.stride(0),
+            _ptr(block_table), block_table.shape[0], block_table.stride(0), int(block_size), int(num_blocks),
+            _ptr(out), out.stride(0), _stream(dev, stream))
+    _check(st, "gcache_convert_req_index_to_global_index")
+    return out

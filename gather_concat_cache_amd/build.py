@@ -20,7 +20,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libgcache.so")
-SOURCES = ["ds_mla_kernels.hip", "nvfp4_kv_kernels.hip", "gcache_abi.hip"]
+SOURCES = ["ds_mla_kernels.hip", "nvfp4_kv_kernels.hip", "sparse_index.hip", "gcache_abi.hip"]
 HEADERS = ["gcache_device.h", "gcache_internal.h"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")

@@ -250,6 +250,45 @@ int gcache_cache_gather_upconvert_fp8_ds_mla(const void* src_cache, void* dst,
                      entry_stride, stream);
 }
 
+int gcache_convert_req_index_to_global_index(const int32_t* req_id, int64_t num_req_id,
+                                             const int32_t* token_indices, int64_t num_tokens,
+                                             int32_t topk, int64_t token_indices_stride,
+                                             const int32_t* block_table, int32_t batch_size,
+                                             int64_t block_table_stride, int32_t block_size,
+                                             int64_t num_blocks, int32_t* out, int64_t out_stride,
+                                             hipStream_t stream) {
+    // the length check of the pages: one request id per token row, exactly
+    if (num_req_id != num_tokens || num_tokens < 0 || topk < 0) return GCACHE_ERR_SHAPE;
+    if (num_tokens == 0 || topk == 0) return GCACHE_OK;
+    if (!req_id || !token_indices || !block_table || !out) return GCACHE_ERR_NULL;
+    if (token_indices_stride < topk || out_stride < topk || batch_size <= 0 ||
+        block_table_stride <= 0 || block_size <= 0 || num_blocks < 0)
+        return GCACHE_ERR_SHAPE;
+    int64_t slots;
+    if (!mul_ok(num_blocks, block_size, &slots) || slots > INT32_MAX) return GCACHE_ERR_SHAPE;
+    if (!aligned(req_id, 4) || !aligned(token_indices, 4) || !aligned(block_table, 4) || !aligned(out, 4))
+        return GCACHE_ERR_ALIGN;
+    int rc = check_device();
+    if (rc) return rc;
+    SparseIndexParams p;
+    p.req_id = req_id;
+    p.token_indices = token_indices;
+    p.out = out;
+    p.num_tokens = num_tokens;
+    p.ti_stride = token_indices_stride;
+    p.out_stride = out_stride;
+    p.topk = topk;
+    p.waves_per_row = (topk + 4 * kWave - 1) / (4 * kWave);
+    p.vec16 = topk % 4 == 0 && token_indices_stride % 4 == 0 && out_stride % 4 == 0 &&
+              aligned(token_indices, 16) && aligned(out, 16);
+    p.block_table = block_table;
+    p.bt_stride = block_table_stride;
+    p.batch = batch_size;
+    p.num_blocks = num_blocks;
+    p.div = make_div(block_size);
+    return launched(launch_convert_req_index(p, stream));
+}
+
 int gcache_context_chunk_plan(const int32_t* context_lens, int32_t batch_size,
                               int64_t workspace_rows, int32_t block_size,
                               int32_t* chunk_rows, int32_t* num_chunks) {

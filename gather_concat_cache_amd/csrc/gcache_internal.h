@@ -74,6 +74,21 @@ struct KvGatherParams {
     const float* gscale[2];
 };
 
+struct SparseIndexParams {
+    const int32_t* req_id;       // [num_tokens]
+    const int32_t* token_indices;// [num_tokens, >=topk], row stride ti_stride
+    int32_t* out;                // [num_tokens, >=topk], row stride out_stride
+    int64_t num_tokens, ti_stride, out_stride;
+    int32_t topk;
+    int32_t waves_per_row;       // ceil(topk / 256)
+    int32_t vec16;               // 16-byte path allowed
+    const int32_t* block_table;
+    int64_t bt_stride;
+    int32_t batch;
+    int64_t num_blocks;
+    BlockDiv div;
+};
+
 hipError_t launch_write_nvfp4_ds_mla(const DsMlaWriteParams& p, hipStream_t s);
 hipError_t launch_write_fp8_ds_mla(const DsMlaWriteParams& p, hipStream_t s);
 hipError_t launch_gather_nvfp4_ds_mla(const DsMlaGatherParams& p, hipStream_t s);
@@ -81,6 +96,7 @@ hipError_t launch_gather_fp8_ds_mla(const DsMlaGatherParams& p, hipStream_t s);
 hipError_t launch_gather_bf16(const DsMlaGatherParams& p, hipStream_t s);
 hipError_t launch_reshape_and_cache_nvfp4(const KvWriteParams& p, hipStream_t s);
 hipError_t launch_gather_nvfp4_kv(const KvGatherParams& p, hipStream_t s);
+hipError_t launch_convert_req_index(const SparseIndexParams& p, hipStream_t s);
 
 // Launch `waves` one-shot waves of `kernel(params, wave0)`: the kernel's
 // wave index is wave0 + blockIdx.x * kWavesPerBlock + wave_id().  Grids are

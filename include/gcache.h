@@ -211,6 +211,33 @@ int gcache_cache_gather_bf16(const void* src_cache, void* dst, int64_t total_tok
                              hipStream_t stream);
 
 /*
+ * Sparse index conversion (triton_convert_req_index_to_global_index) --
+ * [PR48642] "Implementation breakdown" item 1: a call whose req_id and
+ * token_indices lengths differ is rejected (GCACHE_ERR_SHAPE) instead of
+ * running past the shorter one.  For token row t and k < topk, with
+ * i = token_indices[t, k] (a position in request req_id[t]'s context):
+ *     out[t, k] = block_table[req_id[t], i / block_size] * block_size
+ *                 + i % block_size                      (a global slot id)
+ * and -1 when i < 0, req_id[t] is outside [0, batch_size), i / block_size
+ * >= block_table_stride, or the block id is outside [0, num_blocks).
+ *
+ *  req_id         int32 [num_req_id]   (device)
+ *  token_indices  int32 [num_tokens, >=topk], row stride in elements
+ *  block_table    int32 [batch_size, block_table_stride]
+ *  out            int32 [num_tokens, >=topk], row stride in elements
+ * Requirements: num_req_id == num_tokens, num_blocks * block_size <=
+ * INT32_MAX, 4-byte aligned arrays (rows 16-byte aligned with topk % 4 == 0
+ * take the vector path).  num_tokens == 0 or topk == 0 is a no-op.
+ */
+int gcache_convert_req_index_to_global_index(const int32_t* req_id, int64_t num_req_id,
+                                             const int32_t* token_indices, int64_t num_tokens,
+                                             int32_t topk, int64_t token_indices_stride,
+                                             const int32_t* block_table, int32_t batch_size,
+                                             int64_t block_table_stride, int32_t block_size,
+                                             int64_t num_blocks, int32_t* out, int64_t out_stride,
+                                             hipStream_t stream);
+
+/*
  * Chunked-context plan -- [PR48642] "Key source excerpts"
  * (_compute_prefill_context): a prefill whose cached context does not fit
  * the bf16 workspace gathers it in chunks; chunk i runs the gather with

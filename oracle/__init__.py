@@ -64,6 +64,7 @@ def lib():
                                 _I64, _I64],
             "orc_gather_walk": [_I64, _P, _I64, _P, _P, _I32, _I64, _I32, _P, _P],
             "orc_context_chunk_plan": [_P, _I32, _I64, _I32, _P, _P],
+            "orc_convert_req_index": [_P, _I64, _P, _I64, _I32, _I64, _P, _I32, _I64, _I32, _I64, _P, _I64],
             "orc_context_chunk": [_P, _I32, _I32, _I32, _P, _P, _P],
             "orc_kv_layout_split": [_I32, _I32, _I32, C.POINTER(KvLayout)],
             "orc_reshape_and_cache_nvfp4": [_P, _P, _I64, _I64, _I64, _I64, _P, _I64, _P, _I64, _I32,
@@ -310,3 +311,16 @@ def context_chunks(context_lens, workspace_rows, block_size):
                "context_chunk")
         out.append((ss, ws, tot.value))
     return c.value, out
+
+
+def convert_req_index(req_id, token_indices, block_table, block_size, num_blocks):
+    """Sparse index conversion: int32 [T, topk] global slot ids (-1 invalid)."""
+    req_id = _need(np.asarray(req_id, np.int32), np.int32, "req_id")
+    ti = _need(np.asarray(token_indices, np.int32), np.int32, "token_indices")
+    bt = _need(np.asarray(block_table, np.int32), np.int32, "block_table")
+    T, K = ti.shape
+    out = np.zeros((T, K), np.int32)
+    _check(lib().orc_convert_req_index(_ptr(req_id), req_id.shape[0], _ptr(ti), T, K, K, _ptr(bt),
+                                       bt.shape[0], bt.shape[1], int(block_size), int(num_blocks),
+                                       _ptr(out), K), "convert_req_index")
+    return out

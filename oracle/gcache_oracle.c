@@ -731,3 +731,35 @@ int orc_context_chunk(const int32_t* context_lens, int32_t batch_size, int32_t c
     *total_rows = rows;
     return ORC_OK;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Sparse index conversion (vLLM PR #48642 digest, "Implementation           */
+/* breakdown" item 1): token row t's top-k positions, local to request       */
+/* req_id[t], become global slot ids through that request's block table.    */
+/* The call is rejected when req_id and token_indices differ in length.      */
+/* READING: -1 for a negative position, a request id outside [0, batch), a  */
+/* position past the block-table row or a block id outside the cache.       */
+/* ------------------------------------------------------------------------ */
+int orc_convert_req_index(const int32_t* req_id, int64_t num_req_id,
+                          const int32_t* token_indices, int64_t num_tokens, int32_t topk,
+                          int64_t token_indices_stride, const int32_t* block_table,
+                          int32_t batch_size, int64_t block_table_stride, int32_t block_size,
+                          int64_t num_blocks, int32_t* out, int64_t out_stride) {
+    if (num_req_id != num_tokens) return ORC_ERR_ARG;
+    if (num_tokens < 0 || topk < 0 || block_size <= 0 || batch_size <= 0 ||
+        block_table_stride <= 0 || token_indices_stride < topk || out_stride < topk)
+        return ORC_ERR_ARG;
+    for (int64_t t = 0; t < num_tokens; t++) {
+        for (int32_t k = 0; k < topk; k++) {
+            int32_t i = token_indices[t * token_indices_stride + k];
+            int32_t r = req_id[t];
+            int64_t result = -1;
+            if (i >= 0 && r >= 0 && r < batch_size && i / block_size < block_table_stride) {
+                int64_t blk = block_table[(int64_t)r * block_table_stride + i / block_size];
+                if (blk >= 0 && blk < num_blocks) result = blk * block_size + i % block_size;
+            }
+            out[t * out_stride + k] = (int32_t)result;
+        }
+    }
+    return ORC_OK;
+}

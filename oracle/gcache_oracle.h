@@ -177,6 +177,16 @@ int orc_context_chunk(const int32_t* context_lens, int32_t batch_size, int32_t c
                       int32_t chunk, int32_t* seq_starts, int32_t* workspace_starts,
                       int64_t* total_rows);
 
+/* ---- sparse index conversion ---------------------------------------- */
+/* out[t, k] = global slot of position token_indices[t, k] of request
+ * req_id[t] (block_table[req][i / bs] * bs + i % bs), -1 when invalid;
+ * ORC_ERR_ARG when num_req_id != num_tokens. */
+int orc_convert_req_index(const int32_t* req_id, int64_t num_req_id,
+                          const int32_t* token_indices, int64_t num_tokens, int32_t topk,
+                          int64_t token_indices_stride, const int32_t* block_table,
+                          int32_t batch_size, int64_t block_table_stride, int32_t block_size,
+                          int64_t num_blocks, int32_t* out, int64_t out_stride);
+
 #ifdef __cplusplus
 }
 #endif

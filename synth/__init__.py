@@ -246,3 +246,24 @@ def random_write(seed, num_tokens, num_blocks, block_size, pad_count, scale=1.0)
                      bf16_bits(rng.standard_normal((num_tokens, ROPE), dtype=np.float32) * np.float32(scale)),
                      padded_slots(rng, num_blocks * block_size, num_tokens, pad_count),
                      num_blocks, block_size)
+
+
+def sparse_index_case(seed=1006, num_tokens=4096, topk=2048, batch=64, block_size=64, max_ctx=32768):
+    """Top-k index rows of a sparse-attention batch: `batch` requests with
+    context lengths ~ U[1024, max_ctx] and block tables over a shuffle of the
+    cache blocks; every token row belongs to a request (req_id sorted, equal
+    shares) and holds topk positions ~ U[0, context) with 5 % set to -1."""
+    rng = _rng(seed)
+    lens = rng.integers(1024, max_ctx, size=batch, endpoint=True).astype(np.int64)
+    nblk = -(-lens // block_size)
+    num_blocks = int(nblk.sum())
+    perm = rng.permutation(num_blocks).astype(np.int32)
+    bt = np.full((batch, int(-(-max_ctx // block_size))), -1, np.int32)
+    pos = 0
+    for b in range(batch):
+        bt[b, :nblk[b]] = perm[pos:pos + nblk[b]]
+        pos += int(nblk[b])
+    req = np.sort(rng.integers(0, batch, size=num_tokens)).astype(np.int32)
+    idx = (rng.random((num_tokens, topk)) * lens[req][:, None]).astype(np.int32)
+    idx[rng.random((num_tokens, topk)) < 0.05] = -1
+    return req, idx, bt, block_size, num_blocks

@@ -348,6 +348,43 @@ def test_chunked_context_gather(g, orc, fmt):
     assert_same(got, want, f"chunked {fmt} gather")
 
 
+def test_sparse_index_conversion(g, orc):
+    """Hand vectors, random rows on the element path (topk % 4 != 0,
+    strided input and output) and the vector path, invalid entries, the
+    length check, and the full decode-batch shape (4096 x 2048)."""
+    from conftest import load_golden
+    gv = load_golden("sparse_index_vectors.json")
+    for case in gv["cases"]:
+        out = g.convert_req_index_to_global_index(dev(np.array(gv["req_id"], np.int32)),
+                                                  dev(np.array(gv["token_indices"], np.int32)),
+                                                  dev(np.array(gv["block_table"], np.int32)),
+                                                  gv["block_size"], case["num_blocks"])
+        assert host(out).tolist() == case["out"]
+    rng = np.random.default_rng(71)
+    for K, vec in ((37, False), (256, True), (300, False), (1024, True)):
+        B, mb, bs, nb, T = 5, 9, 16, 60, 50
+        bt = rng.integers(-2, nb + 3, size=(B, mb)).astype(np.int32)
+        req = rng.integers(-1, B + 2, size=T).astype(np.int32)
+        ti = rng.integers(-3, mb * bs + 5, size=(T, K)).astype(np.int32)
+        want = orc.convert_req_index(req, ti, bt, bs, nb)
+        wide = np.zeros((T, K + 5), np.int32)
+        wide[:, :K] = ti
+        ti_dev = dev(ti) if vec else dev(wide)[:, :K]
+        out = torch.full((T, K + 3), 7, dtype=torch.int32, device="cuda")
+        got = g.convert_req_index_to_global_index(dev(req), ti_dev, dev(bt), bs, nb,
+                                                  out=out if not vec else None)
+        torch.cuda.synchronize()
+        assert_same(host(got)[:, :K], want, f"sparse index K={K}")
+        if not vec:
+            assert np.all(host(out)[:, K:] == 7)          # bytes past topk untouched
+    with pytest.raises(g.GcacheError):                    # req_id one longer than the rows
+        g.convert_req_index_to_global_index(dev(np.zeros(6, np.int32)), dev(np.zeros((5, 8), np.int32)),
+                                            dev(np.zeros((1, 1), np.int32)), 16, 1)
+    req, idx, bt, bs, nb = synth.sparse_index_case()
+    got = g.convert_req_index_to_global_index(dev(req), dev(idx), dev(bt), bs, nb)
+    assert_same(host(got), orc.convert_req_index(req, idx, bt, bs, nb), "sparse index 4096 x 2048")
+
+
 # ---------------------------------------------------------------------------
 # per-head NVFP4 K/V
 # ---------------------------------------------------------------------------
