@@ -11,12 +11,12 @@ from ._native import (FP8_DS_MLA, LIB_PATH, NVFP4_DS_MLA, GcacheError, NvFp4KvLa
                       cache_write_fp8_ds_mla, cache_write_nvfp4_ds_mla, context_chunks,
                       convert_req_index_to_global_index, entry_bytes,
                       gather_context_chunked,
-                      gather_upconvert_nvfp4_kv, load, nvfp4_full_dim, nvfp4_kv_split_layout,
+                      gather_upconvert_nvfp4_kv, load, nvfp4_full_dim, nvfp4_kv_split_layout, nvfp4_kv_split_views,
                       reshape_and_cache_nvfp4)
 
 __all__ = [
     "NVFP4_DS_MLA", "FP8_DS_MLA", "LIB_PATH", "GcacheError", "NvFp4KvLayout", "load",
-    "entry_bytes", "nvfp4_full_dim", "nvfp4_kv_split_layout",
+    "entry_bytes", "nvfp4_full_dim", "nvfp4_kv_split_layout", "nvfp4_kv_split_views",
     "cache_write_nvfp4_ds_mla", "cache_write_fp8_ds_mla",
     "cache_gather_upconvert_nvfp4_ds_mla", "cache_gather_upconvert_fp8_ds_mla", "cache_gather_bf16",
     "reshape_and_cache_nvfp4", "gather_upconvert_nvfp4_kv",

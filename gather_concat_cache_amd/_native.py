@@ -50,6 +50,7 @@ _SIGS = {
     "gcache_cache_gather_bf16": (C.c_int, [_P, _P, _I64, _I64, _P, _I64, _P, _P, _I32, _I64, _I32, _I64,
                                            _I64, _P]),
     "gcache_nvfp4_kv_split_layout": (C.c_int, [_I32, _I32, _I32, C.POINTER(NvFp4KvLayout)]),
+    "gcache_nvfp4_kv_split_layout_hnd": (C.c_int, [_I32, _I32, _I32, C.POINTER(NvFp4KvLayout)]),
     "gcache_context_chunk_plan": (C.c_int, [_P, _I32, _I64, _I32, _P, _P]),
     "gcache_convert_req_index_to_global_index": (C.c_int, [_P, _I64, _P, _I64, _I32, _I64, _P, _I32, _I64,
                                                            _I32, _I64, _P, _I64, _P]),
@@ -114,11 +115,46 @@ def nvfp4_full_dim(head_size):
     return load().gcache_nvfp4_full_dim(head_size)
 
 
-def nvfp4_kv_split_layout(block_size, num_heads, head_size):
+def nvfp4_kv_split_layout(block_size, num_heads, head_size, hnd=False):
+    """Split per-head NVFP4 layout (data rows then scale rows in each side),
+    NHD token-major, or HND head-major with hnd=True."""
     L = NvFp4KvLayout()
-    _check(load().gcache_nvfp4_kv_split_layout(block_size, num_heads, head_size, C.byref(L)),
-           "nvfp4_kv_split_layout")
+    name = "gcache_nvfp4_kv_split_layout_hnd" if hnd else "gcache_nvfp4_kv_split_layout"
+    _check(getattr(load(), name)(block_size, num_heads, head_size, C.byref(L)), name)
     return L
+
+
+def nvfp4_kv_split_views(kv_cache, num_heads, head_size, layout=None):
+    """Views of a per-head NVFP4 cache (uint8, num_blocks x block_size
+    given by kv_cache.shape[0] and kv_cache.shape[2] of the
+    (num_blocks, 2, block_size, num_heads, full_dim) allocation):
+    ([k_data, v_data], [k_scale, v_scale]) as uint8 [num_blocks, block_size,
+    num_heads, head_size/2] and float8_e4m3fn [num_blocks, block_size,
+    num_heads, head_size/16] over the same bytes, for any layout (default
+    the NHD split layout).  Works on CPU and GPU tensors alike."""
+    if kv_cache.dtype != torch.uint8 or kv_cache.dim() != 5:
+        raise ValueError("kv_cache must be uint8 [num_blocks, 2, block_size, num_heads, full_dim]")
+    nb, bs = kv_cache.shape[0], kv_cache.shape[2]
+    if layout is None:
+        layout = nvfp4_kv_split_layout(bs, num_heads, head_size)
+    base = kv_cache.as_strided((kv_cache.untyped_storage().nbytes() - kv_cache.storage_offset(),), (1,))
+    need = (nb - 1) * layout.block_stride + layout.side_stride + max(
+        layout.data_offset + (bs - 1) * layout.data_token_stride + (num_heads - 1) * layout.data_head_stride
+        + head_size // 2,
+        layout.scale_offset + (bs - 1) * layout.scale_token_stride + (num_heads - 1) * layout.scale_head_stride
+        + head_size // 16) if nb else 0
+    if need > base.numel():
+        raise ValueError("layout reaches past the cache allocation")
+    data, scale = [], []
+    for side in (0, 1):
+        o = side * layout.side_stride
+        data.append(base.as_strided((nb, bs, num_heads, head_size // 2),
+                                    (layout.block_stride, layout.data_token_stride, layout.data_head_stride, 1),
+                                    base.storage_offset() + o + layout.data_offset))
+        scale.append(base.as_strided((nb, bs, num_heads, head_size // 16),
+                                     (layout.block_stride, layout.scale_token_stride, layout.scale_head_stride, 1),
+                                     base.storage_offset() + o + layout.scale_offset).view(torch.float8_e4m3fn))
+    return data, scale
 
 
 # ---------------------------------------------------------------------------

@@ -362,6 +362,24 @@ int gcache_nvfp4_kv_split_layout(int32_t block_size, int32_t num_heads, int32_t 
     return GCACHE_OK;
 }
 
+int gcache_nvfp4_kv_split_layout_hnd(int32_t block_size, int32_t num_heads, int32_t head_size,
+                                     gcache_nvfp4_kv_layout* out) {
+    if (!out) return GCACHE_ERR_NULL;
+    if (block_size <= 0 || num_heads <= 0 || head_size <= 0 || head_size % 16)
+        return GCACHE_ERR_SHAPE;
+    const int64_t data_row = head_size / 2, scale_row = head_size / 16;
+    const int64_t side = (int64_t)block_size * num_heads * (data_row + scale_row);
+    out->data_offset = 0;
+    out->data_token_stride = data_row;                       // heads outermost
+    out->data_head_stride = (int64_t)block_size * data_row;
+    out->scale_offset = (int64_t)num_heads * block_size * data_row;
+    out->scale_token_stride = scale_row;
+    out->scale_head_stride = (int64_t)block_size * scale_row;
+    out->side_stride = side;
+    out->block_stride = 2 * side;
+    return GCACHE_OK;
+}
+
 int gcache_reshape_and_cache_nvfp4(const void* key, const void* value, int64_t key_token_stride,
                                    int64_t key_head_stride, int64_t value_token_stride,
                                    int64_t value_head_stride, void* kv_cache,

@@ -293,6 +293,14 @@ typedef struct {
 int gcache_nvfp4_kv_split_layout(int32_t block_size, int32_t num_heads, int32_t head_size,
                                  gcache_nvfp4_kv_layout* out);
 
+/* The same split layout in HND order ([PR37332] "Key source excerpts": the
+ * split views keep the cache's NHD or HND order): inside each side, data
+ * rows [num_heads][block_size][head_size/2] then scale rows
+ * [num_heads][block_size][head_size/16]; same block_stride.  Returns
+ * GCACHE_ERR_SHAPE for bad sizes. */
+int gcache_nvfp4_kv_split_layout_hnd(int32_t block_size, int32_t num_heads, int32_t head_size,
+                                     gcache_nvfp4_kv_layout* out);
+
 /*
  * Per-head NVFP4 write (reshape_and_cache_nvfp4) -- [PR37332]
  * "Implementation breakdown" item 4.

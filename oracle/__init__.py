@@ -67,6 +67,7 @@ def lib():
             "orc_convert_req_index": [_P, _I64, _P, _I64, _I32, _I64, _P, _I32, _I64, _I32, _I64, _P, _I64],
             "orc_context_chunk": [_P, _I32, _I32, _I32, _P, _P, _P],
             "orc_kv_layout_split": [_I32, _I32, _I32, C.POINTER(KvLayout)],
+            "orc_kv_layout_split_hnd": [_I32, _I32, _I32, C.POINTER(KvLayout)],
             "orc_reshape_and_cache_nvfp4": [_P, _P, _I64, _I64, _I64, _I64, _P, _I64, _P, _I64, _I32,
                                             _I32, _I64, _I32, C.POINTER(KvLayout), _F32, _F32],
             "orc_gather_upconvert_nvfp4_kv": [_P, _I64, _P, _P, _I64, _I64, _I64, _I64, _I64, _P,
@@ -76,7 +77,7 @@ def lib():
         for name, args in sig.items():
             fn = getattr(L, name)
             fn.argtypes = args
-            fn.restype = None if name.endswith("_array") or name == "orc_kv_layout_split" else C.c_int
+            fn.restype = None if name.endswith("_array") or name.startswith("orc_kv_layout_split") else C.c_int
         for name in ("orc_nvfp4_ds_mla_entry_bytes", "orc_fp8_ds_mla_entry_bytes"):
             getattr(L, name).restype = C.c_int64
             getattr(L, name).argtypes = []
@@ -255,9 +256,10 @@ def gather_walk(total_tokens, block_table, workspace_starts, seq_starts, num_blo
 
 
 # ---- per-head NVFP4 K/V ----------------------------------------------------
-def kv_layout_split(block_size, num_heads, head_size):
+def kv_layout_split(block_size, num_heads, head_size, hnd=False):
     L = KvLayout()
-    lib().orc_kv_layout_split(block_size, num_heads, head_size, C.byref(L))
+    fn = lib().orc_kv_layout_split_hnd if hnd else lib().orc_kv_layout_split
+    fn(block_size, num_heads, head_size, C.byref(L))
     return L
 
 

@@ -541,6 +541,27 @@ void orc_kv_layout_split(int32_t block_size, int32_t num_heads, int32_t head_siz
     out->block_stride = 2 * side;
 }
 
+/* HND order of the split layout: within a side, head h's data rows for all
+ * token offsets come before head h+1's, then the scale rows in the same
+ * order (vLLM PR #37332 digest, "Key source excerpts": the split views keep
+ * NHD or HND).  Written as sizes of the nested regions. */
+void orc_kv_layout_split_hnd(int32_t block_size, int32_t num_heads, int32_t head_size,
+                             orc_kv_layout* out) {
+    int64_t data_row = head_size / 2, scale_row = head_size / 16;
+    int64_t data_per_head = block_size * data_row;          /* one head, all offsets */
+    int64_t scale_per_head = block_size * scale_row;
+    int64_t data_region = num_heads * data_per_head;
+    int64_t scale_region = num_heads * scale_per_head;
+    out->data_offset = 0;
+    out->data_head_stride = data_per_head;
+    out->data_token_stride = data_row;
+    out->scale_offset = data_region;
+    out->scale_head_stride = scale_per_head;
+    out->scale_token_stride = scale_row;
+    out->side_stride = data_region + scale_region;
+    out->block_stride = 2 * out->side_stride;
+}
+
 static int check_kv_args(int64_t num_tokens, int32_t num_heads, int32_t head_size,
                          int64_t num_blocks, int32_t block_size, const orc_kv_layout* L,
                          int64_t cache_bytes, float k_scale, float v_scale) {

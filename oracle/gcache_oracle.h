@@ -141,6 +141,8 @@ typedef struct {
  * all data rows followed by all scale rows, token-major). */
 void orc_kv_layout_split(int32_t block_size, int32_t num_heads, int32_t head_size,
                          orc_kv_layout* out);
+void orc_kv_layout_split_hnd(int32_t block_size, int32_t num_heads, int32_t head_size,
+                             orc_kv_layout* out);
 
 /* key/value: bf16 bits [num_tokens, num_heads, head_size] with the given
  * token and head strides (elements); k_scale / v_scale: per-tensor fp32. */

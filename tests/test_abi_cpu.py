@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(lib):
         "gcache_cache_gather_upconvert_nvfp4_ds_mla", "gcache_cache_gather_upconvert_fp8_ds_mla",
         "gcache_cache_gather_bf16", "gcache_context_chunk_plan", "gcache_context_chunk",
         "gcache_convert_req_index_to_global_index",
-        "gcache_nvfp4_kv_split_layout", "gcache_reshape_and_cache_nvfp4",
+        "gcache_nvfp4_kv_split_layout", "gcache_nvfp4_kv_split_layout_hnd", "gcache_reshape_and_cache_nvfp4",
         "gcache_gather_upconvert_nvfp4_kv"]), names
     for n in names:
         assert hasattr(lib, n), f"{n} not exported by libgcache.so"

@@ -439,9 +439,9 @@ def test_perhead_config5(g, orc):
            w.k_scale, w.v_scale)
 
 
-@pytest.mark.parametrize("variant", ["interleaved", "hnd", "odd-head-size", "strided-input"])
+@pytest.mark.parametrize("variant", ["interleaved", "hnd", "hnd-split", "odd-head-size", "strided-input"])
 def test_perhead_layouts(g, orc, variant):
-    seed = {"interleaved": 41, "hnd": 42, "odd-head-size": 43, "strided-input": 44}[variant]
+    seed = {"interleaved": 41, "hnd": 42, "hnd-split": 45, "odd-head-size": 43, "strided-input": 44}[variant]
     rng = np.random.default_rng(seed)
     # head size 80: 5 scale blocks and 10 chunks per head (the non-power-of-two paths)
     # interleaved [data | scales] rows keep 8-byte data alignment at head size 128 (72-byte rows)
@@ -458,9 +458,13 @@ def test_perhead_layouts(g, orc, variant):
         kw = dict(data_offset=0, data_token_stride=hs // 2, data_head_stride=bs * hs // 2,
                   scale_offset=bs * H * hs // 2, scale_token_stride=hs // 16,
                   scale_head_stride=bs * hs // 16, side_stride=bs * H * fd, block_stride=2 * bs * H * fd)
+    elif variant == "hnd-split":        # each side's layout from the library's and the oracle's HND helpers
+        kw = orc.kv_layout_split(bs, H, hs, hnd=True).as_dict()
     else:
         kw = orc.kv_layout_split(bs, H, hs).as_dict()
     L_orc, L_gpu = orc.KvLayout(**kw), g.NvFp4KvLayout(**kw)
+    if variant == "hnd-split":
+        L_gpu = g.nvfp4_kv_split_layout(bs, H, hs, hnd=True)
     kd = vd = None
     if variant == "strided-input":      # key / value as slices of a wider [T, H, hs + 16] buffer
         big = np.zeros((T, H, hs + 16), np.uint16)
@@ -512,3 +516,28 @@ def test_perhead_out_of_range_metadata(g, orc):
     torch.cuda.synchronize()
     assert_same(host(ko), ek, "per-head gather K with out-of-range metadata")
     assert_same(host(vo), ev, "per-head gather V with out-of-range metadata")
+
+
+def test_perhead_split_views_on_device(g, orc):
+    """The split views of a device cache written through the HND layout hold
+    the bytes the oracle writes (data as uint8, scales as float8_e4m3fn)."""
+    rng = np.random.default_rng(46)
+    H, hs, nb, bs, T = 4, 64, 10, 16, 100
+    key, value, slots = _kv_case(rng, T, H, hs, nb, bs, 5)
+    ks, vs = synth.global_scale(key), synth.global_scale(value)
+    L = orc.kv_layout_split(bs, H, hs, hnd=True)
+    fd = hs // 2 + hs // 16
+    want = np.zeros(nb * 2 * bs * H * fd, np.uint8)
+    orc.reshape_and_cache_nvfp4(key, value, want, slots, nb, bs, L, ks, vs)
+    cache5 = torch.zeros((nb, 2, bs, H, fd), dtype=torch.uint8, device="cuda")
+    Lg = g.nvfp4_kv_split_layout(bs, H, hs, hnd=True)
+    g.reshape_and_cache_nvfp4(dev(key), dev(value), cache5, dev(slots),
+                              torch.tensor([ks], dtype=torch.float32, device="cuda"),
+                              torch.tensor([vs], dtype=torch.float32, device="cuda"), layout=Lg)
+    torch.cuda.synchronize()
+    dv, sv = g.nvfp4_kv_split_views(cache5, H, hs, Lg)
+    dh, sh = g.nvfp4_kv_split_views(torch.from_numpy(want).view(nb, 2, bs, H, fd), H, hs, Lg)
+    for side in (0, 1):
+        assert_same(host(dv[side].contiguous()), dh[side].contiguous().numpy(), f"data view side {side}")
+        assert_same(host(sv[side].view(torch.uint8).contiguous()), sh[side].view(torch.uint8).contiguous().numpy(),
+                    f"scale view side {side}")
