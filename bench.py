@@ -442,7 +442,7 @@ def write_traffic(fetch_dir, write_dir):
     cal_f = ", ".join(f"{v:,.0f}" for v in fetch["calibration"])
     cal_w = ", ".join(f"{v:,.0f}" for v in write["calibration"])
     run = ("timeout -s KILL 120 rocprofv3 --pmc {c} --kernel-trace -f csv -d $R/{d} -o bench -- python3 "
-           "$R/bench.py --steps 3 --warmup 1 --no-cpu-baseline --copy-calibration 1024")
+           "$R/bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-extras --copy-calibration 1024")
     md = ["# HBM traffic per launch — all six kernels, prefill-context pass workload", "",
           "Two counter runs (one counter each), from /tmp on the MI355X box with the repository at $R, "
           "then the host-side summary:", "", "```",
@@ -475,7 +475,7 @@ def write_stats(prof_dir, bench_json):
     (path,) = glob.glob(os.path.join(prof_dir, "*kernel_stats.csv"))
     rows = list(csv.DictReader(open(path)))
     cmd = ("rocprofv3 --kernel-trace --stats -f csv -d $R/" + os.path.relpath(prof_dir, ROOT) +
-           " -o bench -- python3 $R/bench.py --steps 20 --warmup 3 --no-cpu-baseline")
+           " -o bench -- python3 $R/bench.py --steps 20 --warmup 3 --no-cpu-baseline --no-extras")
     md = ["# rocprofv3 kernel statistics — all six kernels, prefill-context pass workload", "",
           "Command (from /tmp on the MI355X box, repository at $R), then the host-side summary:", "",
           "```", cmd, f"python3 bench.py --stats-from {os.path.relpath(prof_dir, ROOT)}"
