@@ -20,8 +20,9 @@
 //     lines written by several instructions;
 //   - inputs and outputs use streaming (nontemporal) accesses.
 // Mappings:
-//   nvfp4 write : one lane per 16-value NoPE block (32 B in, 8 B + 1 scale
-//                 byte staged), 32 lanes per token; no cross-lane reduction.
+//   nvfp4 write : 8 values per lane (one 16 B load, one contiguous 1 KiB
+//                 load per token), one token per 64 lanes; a 16-value block
+//                 spans two lanes, joined by one DPP swap.
 //   fp8 write   : 8 values per lane (one 16 B load), one token per 64 lanes;
 //                 the 128-value group amax is a 4-step DPP butterfly inside
 //                 each 16-lane row.
@@ -65,78 +66,90 @@ __device__ __forceinline__ void store_staged(const DsMlaWriteParams& p, const ui
     }
 }
 
-// nvfp4_ds_mla: lane j of each half-wave quantizes NoPE block j (values
-// 16j..16j+15) and RoPE pair j of one token; wave w stages tokens
-// w*kTokPerWave .. +kTokPerWave-1 of the group, two per pass.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// nvfp4_ds_mla: wave w stages tokens w, w+4, ... of the group, one token per
+// 64 lanes: lane l loads NoPE values 8l..8l+7 (one 16 B load, so each token
+// is one contiguous 1 KiB load), block l/2's amax joins the two halves of
+// the block with one DPP swap of adjacent lanes, both lanes derive the same
+// scale and each packs its 4 code bytes.  RoPE: lanes 8i..8i+7 convert
+// token w+4i's 64 values, 8 per lane.
 __global__ __launch_bounds__(kBlockThreads) void k_write_nvfp4_ds_mla(DsMlaWriteParams p, int64_t group0) {
-    constexpr int kPasses = kTokPerWave / 2;
+    static_assert(kTokPerWave <= 8, "RoPE conversion uses 8 lanes per token");
     __shared__ __align__(16) uint8_t s_ent[kWriteTile * kNvEntry];
     __shared__ int64_t s_addr[kWriteTile];
     const int lane = lane_id(), w = wave_id();
-    const int half = lane >> 5, j = lane & 31;
     const int64_t t0 = (group0 + blockIdx.x) * kWriteTile;
     if (t0 >= p.num_tokens) return;                      // workgroup-uniform
 
-    int64_t slot[kPasses];
-    uint4 v0[kPasses], v1[kPasses];
-    uint32_t rw[kPasses];
+    int64_t slot[kTokPerWave];                           // wave-uniform
+    uint4 v[kTokPerWave];
 #pragma unroll
-    for (int i = 0; i < kPasses; i++) {
-        const int64_t t = t0 + w * kTokPerWave + 2 * i + half;
+    for (int i = 0; i < kTokPerWave; i++) {
+        const int64_t t = t0 + w + kWavesPerBlock * i;
         slot[i] = t < p.num_tokens ? valid_slot(p.slots[t], p.num_slots) : -1;
     }
 #pragma unroll
-    for (int i = 0; i < kPasses; i++) {                  // all loads first; padding reads nothing
-        if (slot[i] < 0) continue;
-        const int64_t t = t0 + w * kTokPerWave + 2 * i + half;
-        const uint8_t* row = reinterpret_cast<const uint8_t*>(p.kv_c + t * p.kv_c_stride) + 32 * j;
-        v0[i] = ld_stream16(row);
-        v1[i] = ld_stream16(row + 16);
-        rw[i] = ld_stream4(reinterpret_cast<const uint8_t*>(p.k_pe + t * p.k_pe_stride) + 4 * j);
-    }
+    for (int i = 0; i < kTokPerWave; i++)                // all loads first; padding reads nothing
+        if (slot[i] >= 0)
+            v[i] = ld_stream16(reinterpret_cast<const uint8_t*>(
+                                   p.kv_c + (t0 + w + kWavesPerBlock * i) * p.kv_c_stride) + 16 * lane);
+    const int ri = lane >> 3, rc = lane & 7;
+    int64_t rslot = -1;
 #pragma unroll
-    for (int i = 0; i < kPasses; i++) {
-        const int k = w * kTokPerWave + 2 * i + half;
-        if (j == 0) s_addr[k] = slot_entry(p, slot[i]);
-        if (slot[i] < 0) continue;
-        const uint32_t wv[8] = {v0[i].x, v0[i].y, v0[i].z, v0[i].w, v1[i].x, v1[i].y, v1[i].z, v1[i].w};
-        float x[16];
+    for (int i = 0; i < kTokPerWave; i++)
+        if (ri == i) rslot = slot[i];
+    uint4 r = make_uint4(0, 0, 0, 0);
+    if (rslot >= 0)
+        r = ld_stream16(reinterpret_cast<const uint8_t*>(
+                            p.k_pe + (t0 + w + kWavesPerBlock * ri) * p.k_pe_stride) + 16 * rc);
+
 #pragma unroll
-        for (int q = 0; q < 8; q++) {
+    for (int i = 0; i < kTokPerWave; i++) {
+        const int k = w + kWavesPerBlock * i;
+        if (lane == 0) s_addr[k] = slot_entry(p, slot[i]);
+        if (slot[i] < 0) continue;                       // wave-uniform: DPP below sees all lanes
+        const uint32_t wv[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+        float x[8];
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
             x[2 * q] = bf16_lo(wv[q]);
             x[2 * q + 1] = bf16_hi(wv[q]);
         }
         float amax = 0.0f;
 #pragma unroll
-        for (int q = 0; q < 16; q++) amax = fmaxf(amax, fabsf(x[q]));
+        for (int q = 0; q < 8; q++) amax = fmaxf(amax, fabsf(x[q]));
+        amax = fmaxf(amax, dpp_f32<0xB1>(amax));    // quad_perm [1,0,3,2]: the other half of the block
         // Block scale: e4m3_rn_sat(amax / 6), then the binary32 reciprocal
         // of its decoded value (0 for a zero scale).
         const uint32_t sf = put_e4m3x2<false>(0u, amax / 6.0f, 0.0f) & 0xFFu;
         const float s = e4m3_f32(sf);
         const float inv = (s == 0.0f) ? 0.0f : 1.0f / s;
-        uint32_t q0 = 0, q1 = 0;
+        uint32_t q0 = 0;
         q0 = put_e2m1x2<0>(q0, x[0] * inv, x[1] * inv);
         q0 = put_e2m1x2<1>(q0, x[2] * inv, x[3] * inv);
         q0 = put_e2m1x2<2>(q0, x[4] * inv, x[5] * inv);
         q0 = put_e2m1x2<3>(q0, x[6] * inv, x[7] * inv);
-        q1 = put_e2m1x2<0>(q1, x[8] * inv, x[9] * inv);
-        q1 = put_e2m1x2<1>(q1, x[10] * inv, x[11] * inv);
-        q1 = put_e2m1x2<2>(q1, x[12] * inv, x[13] * inv);
-        q1 = put_e2m1x2<3>(q1, x[14] * inv, x[15] * inv);
-        const uint32_t rq = put_e4m3x2<false>(0u, bf16_lo(rw[i]), bf16_hi(rw[i]));
         uint8_t* e = s_ent + k * kNvEntry;
-        *reinterpret_cast<uint2*>(e + 8 * j) = make_uint2(q0, q1);
-        *reinterpret_cast<uint16_t*>(e + kNvRopeOff + 2 * j) = (uint16_t)rq;
-        e[kNvScaleOff + j] = (uint8_t)sf;
+        *reinterpret_cast<uint32_t*>(e + 4 * lane) = q0;
+        if ((lane & 1) == 0) e[kNvScaleOff + (lane >> 1)] = (uint8_t)sf;
+    }
+    if (rslot >= 0) {                                    // RoPE values 8rc..8rc+7 -> 8 e4m3 bytes
+        uint32_t a = 0, b = 0;
+        a = put_e4m3x2<false>(a, bf16_lo(r.x), bf16_hi(r.x));
+        a = put_e4m3x2<true>(a, bf16_lo(r.y), bf16_hi(r.y));
+        b = put_e4m3x2<false>(b, bf16_lo(r.z), bf16_hi(r.z));
+        b = put_e4m3x2<true>(b, bf16_lo(r.w), bf16_hi(r.w));
+        *reinterpret_cast<uint2*>(s_ent + (w + kWavesPerBlock * ri) * kNvEntry + kNvRopeOff + 8 * rc) =
+            make_uint2(a, b);
     }
     __syncthreads();
     store_staged<kNvEntry>(p, s_ent, s_addr);
 }
 
-template <int CTRL>
-__device__ __forceinline__ float dpp_f32(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
-}
 
 // fp8_ds_mla: 512 e4m3 | 4 x fp32 scale (amax / 448 per 128) | 64 bf16.
 // Wave w stages tokens w, w+4, ... of the group, one token per 64 lanes
