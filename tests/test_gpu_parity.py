@@ -541,3 +541,46 @@ def test_perhead_split_views_on_device(g, orc):
         assert_same(host(dv[side].contiguous()), dh[side].contiguous().numpy(), f"data view side {side}")
         assert_same(host(sv[side].view(torch.uint8).contiguous()), sh[side].view(torch.uint8).contiguous().numpy(),
                     f"scale view side {side}")
+
+
+def test_side_stream_and_graph_replay(g, orc):
+    """Calls enqueued on a side stream (default priority) and a write +
+    gather pair captured in a HIP graph give the oracle's bytes; the graph is
+    replayed several times with eager work in between and every replay is
+    checked (the kernels allocate nothing and issue no memset)."""
+    w, g_tok, _ = synth.config1()
+    want = np.full(8 * 64 * NV, 0xA5, np.uint8)
+    orc.write_nvfp4_ds_mla(w.kv_c, w.k_pe, want, w.slot_mapping, 8, 64)
+    rows = orc.gather_nvfp4_ds_mla(want, g_tok.total_tokens, g_tok.block_table, g_tok.workspace_starts,
+                                   g_tok.seq_starts, 8, 64)
+    kv, pe, sl = dev(w.kv_c), dev(w.k_pe), dev(w.slot_mapping)
+    bt, ws, ss = dev(g_tok.block_table), dev(g_tok.workspace_starts), dev(g_tok.seq_starts)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    cache = filled_cache((8, 64, NV), 0xA5)
+    dst = torch.zeros((g_tok.total_tokens, 576), dtype=torch.bfloat16, device="cuda")
+    with torch.cuda.stream(side):
+        g.cache_write_nvfp4_ds_mla(kv, pe, cache, sl)
+        g.cache_gather_upconvert_nvfp4_ds_mla(cache, dst, bt, ws, ss)
+    side.synchronize()
+    assert_same(host(cache).reshape(-1), want, "side-stream write")
+    assert_same(host(dst), rows, "side-stream gather")
+
+    cache2 = filled_cache((8, 64, NV), 0xA5)
+    dst2 = torch.zeros_like(dst)
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(graph, stream=cap):
+            g.cache_write_nvfp4_ds_mla(kv, pe, cache2, sl)
+            g.cache_gather_upconvert_nvfp4_ds_mla(cache2, dst2, bt, ws, ss)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        cache2.fill_(0xA5)                               # eager work between replays
+        dst2.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert_same(host(cache2).reshape(-1), want, f"graph replay {rep}: write")
+        assert_same(host(dst2), rows, f"graph replay {rep}: gather")
