@@ -45,11 +45,13 @@ _P = C.c_void_p
 _I64, _I32, _F32 = C.c_int64, C.c_int32, C.c_float
 
 
-def lib():
+def lib(path=None):
+    """The oracle library (built on first use).  With `path`, load and return
+    that build of the same sources instead, uncached (the pin tests use it
+    to check that planted mistakes are caught)."""
     global _lib
-    if _lib is None:
-        path = _build.ensure_built()
-        L = C.CDLL(path)
+    if _lib is None or path is not None:
+        L = C.CDLL(path or _build.ensure_built())
         sig = {
             "orc_e2m1_encode_array": [_P, _P, _I64], "orc_e4m3_encode_array": [_P, _P, _I64],
             "orc_f32_to_bf16_array": [_P, _P, _I64], "orc_e4m3_decode_array": [_P, _P, _I64],
@@ -83,6 +85,8 @@ def lib():
             getattr(L, name).argtypes = []
         L.orc_nvfp4_full_dim.restype = C.c_int32
         L.orc_nvfp4_full_dim.argtypes = [C.c_int32]
+        if path is not None:
+            return L
         _lib = L
     return _lib
 
