@@ -15,9 +15,9 @@
 //     faster than the scattered fronts of persistent loops;
 //   - every wave issues all of its loads before it needs them;
 //   - every store is a full 16-byte piece: the odd-sized parts of an entry
-//     (8-byte NoPE codes, scale bytes, 2-byte RoPE codes) are assembled in
-//     LDS first, so the cache sees whole 1 KiB runs instead of partial
-//     lines written by several instructions;
+//     (each lane's NoPE code bytes, scale bytes or fp32 scales, RoPE codes)
+//     are assembled in LDS first, so the cache sees whole 1 KiB runs
+//     instead of partial lines written by several instructions;
 //   - inputs and outputs use streaming (nontemporal) accesses.
 // Mappings:
 //   nvfp4 write : 8 values per lane (one 16 B load, one contiguous 1 KiB
@@ -149,7 +149,6 @@ __global__ __launch_bounds__(kBlockThreads) void k_write_nvfp4_ds_mla(DsMlaWrite
     __syncthreads();
     store_staged<kNvEntry>(p, s_ent, s_addr);
 }
-
 
 // fp8_ds_mla: 512 e4m3 | 4 x fp32 scale (amax / 448 per 128) | 64 bf16.
 // Wave w stages tokens w, w+4, ... of the group, one token per 64 lanes
