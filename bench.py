@@ -41,7 +41,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget-s", type=float, default=20.0,
+    ap.add_argument("--cpu-budget-s", type=float, default=40.0,
                     help="approximate CPU seconds for the oracle baseline sample")
     ap.add_argument("--cold", action="store_true",
                     help="also time every kernel once per run after evicting the caches")
