@@ -47,7 +47,10 @@ def parse():
                     help="also time every kernel once per run after evicting the caches")
     ap.add_argument("--only", default=None, help="comma list of op names to run (profiling aid)")
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip the comparator measured after the timed step (BF16 gather)")
+                    help="skip the extras measured after the timed step (BF16 comparator, chunked "
+                         "context, sparse index conversion)")
+    ap.add_argument("--extras-only", action="store_true",
+                    help="profiling aid: fill the nvfp4 cache once, run only the extras, print them")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run a plain elementwise kernel reading and writing MIB MiB, three "
                          "times, outside the timed region, so HBM counters can be scaled against "
@@ -60,6 +63,8 @@ def parse():
                          "(--steps 20 --warmup 3) into profiles/prefill_pass_all_kernels_stats.md")
     ap.add_argument("--bench-json", default=None, metavar="FILE",
                     help="with --stats-from: a bench.py output line of the same build, tabulated beside")
+    ap.add_argument("--stats-extras", action="store_true",
+                    help="with --stats-from: the run was --extras-only; write profiles/extras_kernels_stats.md")
     return ap.parse_args()
 
 
@@ -102,7 +107,7 @@ def main():
         write_traffic(*args.traffic_from)
         return
     if args.stats_from:
-        write_stats(args.stats_from, args.bench_json)
+        write_stats(args.stats_from, args.bench_json, args.stats_extras)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
@@ -158,6 +163,11 @@ def main():
          lambda: gc.gather_upconvert_nvfp4_kv(d["cache5"], d["ko5"], d["vo5"], d["bt5"], d["ws5"], d["ks5"],
                                               d["vs5"], seq_starts=d["ss5"])),
     ]
+    if args.extras_only:
+        ops[0][3]()                                  # the nvfp4 pre-fill the extras read
+        torch.cuda.synchronize()
+        print(json.dumps({"extras": measure_extras(torch, gc, g3, args.steps, dev_arr, d["cache3"])}), flush=True)
+        return
     if args.only:
         keep = set(args.only.split(","))
         ops = [o for o in ops if o[0] in keep]
@@ -466,23 +476,32 @@ def write_traffic(fetch_dir, write_dir):
     print(json.dumps(out, indent=1))
 
 
-def write_stats(prof_dir, bench_json):
+def write_stats(prof_dir, bench_json, extras=False):
     """Markdown summary of a rocprofv3 --stats run of this script, with the
-    HIP-event figures of a bench.py line of the same build when given."""
+    HIP-event figures of a bench.py line of the same build when given
+    (extras=True: a run with --extras-only)."""
     import csv
     import glob
     from gather_concat_cache_amd.build import source_digest
     (path,) = glob.glob(os.path.join(prof_dir, "*kernel_stats.csv"))
     rows = list(csv.DictReader(open(path)))
+    flags = "--extras-only" if extras else "--no-cpu-baseline --no-extras"
     cmd = ("rocprofv3 --kernel-trace --stats -f csv -d $R/" + os.path.relpath(prof_dir, ROOT) +
-           " -o bench -- python3 $R/bench.py --steps 20 --warmup 3 --no-cpu-baseline --no-extras")
-    md = ["# rocprofv3 kernel statistics — all six kernels, prefill-context pass workload", "",
+           f" -o bench -- python3 $R/bench.py --steps 20 --warmup 3 {flags}")
+    title = ("the bench extras (BF16 comparator, chunked context, sparse index conversion)" if extras
+             else "all six kernels, prefill-context pass workload")
+    what = ("20 timed repetitions of each extra after one nvfp4 pre-fill write. The chunked-context pass "
+            "launches the nvfp4 gather once per chunk (8 chunks), so its calls share that kernel's name; "
+            "the spin kernel holds the queue while the chunk launches are enqueued." if extras else
+            "20 timed + 3 warm-up steps (23 calls per kernel). Workloads: nvfp4_ds_mla write 524288 tokens, "
+            "fp8_ds_mla write 1048576 tokens, nvfp4 gather 161766 rows, fp8 gather 219273 rows, per-head "
+            "write 8192 tokens x 8 heads x 128, per-head gather 8110 rows.")
+    md = [f"# rocprofv3 kernel statistics — {title}", "",
           "Command (from /tmp on the MI355X box, repository at $R), then the host-side summary:", "",
           "```", cmd, f"python3 bench.py --stats-from {os.path.relpath(prof_dir, ROOT)}"
+          + (" --stats-extras" if extras else "")
           + (f" --bench-json {os.path.relpath(bench_json, ROOT)}" if bench_json else ""), "```", "",
-          "20 timed + 3 warm-up steps (23 calls per kernel). Workloads: nvfp4_ds_mla write 524288 tokens, "
-          "fp8_ds_mla write 1048576 tokens, nvfp4 gather 161766 rows, fp8 gather 219273 rows, per-head "
-          f"write 8192 tokens x 8 heads x 128, per-head gather 8110 rows. Library digest {source_digest()}.",
+          f"{what} Library digest {source_digest()}.",
           "", "| Kernel | Calls | Average (ns) | Min (ns) | Max (ns) | % of GPU time |",
           "|---|---|---|---|---|---|"]
     for r in rows:
@@ -491,12 +510,19 @@ def write_stats(prof_dir, bench_json):
                   f"| {float(r['Percentage']):.2f} |")
     if bench_json:
         b = json.load(open(bench_json))
-        md += ["", f"Same-build HIP-event averages from `python bench.py` ({b['steps']} timed steps; "
-               f"whole step {b['value']} GB/s, {100 * b['frac_of_hbm_peak']:.1f} % of 8 TB/s):", "",
-               "| Kernel op | ms | GB/s | % of 8 TB/s |", "|---|---|---|---|"]
-        for k, v in b["kernels"].items():
-            md.append(f"| {k} | {v['ms']:.5f} | {v['GB_per_s']:.0f} | {100 * v['frac_of_hbm_peak']:.1f} |")
-    with open(os.path.join(ROOT, "profiles", "prefill_pass_all_kernels_stats.md"), "w") as f:
+        if extras:
+            md += ["", "Same-build HIP-event figures from `python bench.py --extras-only`:", "",
+                   "| Extra | ms | GB/s | % of 8 TB/s |", "|---|---|---|---|"]
+            for k, v in b["extras"].items():
+                md.append(f"| {k} | {v['ms']:.5f} | {v['GB_per_s']:.0f} | {100 * v['frac_of_hbm_peak']:.1f} |")
+        else:
+            md += ["", f"Same-build HIP-event averages from `python bench.py` ({b['steps']} timed steps; "
+                   f"whole step {b['value']} GB/s, {100 * b['frac_of_hbm_peak']:.1f} % of 8 TB/s):", "",
+                   "| Kernel op | ms | GB/s | % of 8 TB/s |", "|---|---|---|---|"]
+            for k, v in b["kernels"].items():
+                md.append(f"| {k} | {v['ms']:.5f} | {v['GB_per_s']:.0f} | {100 * v['frac_of_hbm_peak']:.1f} |")
+    name = "extras_kernels_stats.md" if extras else "prefill_pass_all_kernels_stats.md"
+    with open(os.path.join(ROOT, "profiles", name), "w") as f:
         f.write("\n".join(md) + "\n")
 
 
