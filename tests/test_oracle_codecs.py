@@ -126,7 +126,7 @@ def test_exhaustive_sweep_against_independent_encoder(tmp_path):
 
 def test_sweep_checker_detects_a_planted_error(tmp_path):
     """The sweep fails when the oracle's e4m3 tie rule is flipped (a mutant
-    oracle built on the CPU): the checker is not vacuous."""
+    oracle built on the CPU): the sweep is not vacuous."""
     src = open(os.path.join(ROOT, "oracle", "gcache_oracle.c")).read()
     mutant = src.replace("return (lo % 2 == 0) ? lo : hi;", "return (lo % 2 == 0) ? hi : lo;")
     assert mutant != src
