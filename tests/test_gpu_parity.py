@@ -385,6 +385,35 @@ def test_sparse_index_conversion(g, orc):
     assert_same(host(got), orc.convert_req_index(req, idx, bt, bs, nb), "sparse index 4096 x 2048")
 
 
+@pytest.mark.parametrize("fmt", ["nvfp4", "fp8"])
+@pytest.mark.parametrize("bs", [1, 3, 512])
+def test_extreme_block_sizes(g, orc, fmt, bs):
+    """Block sizes 1 (every token its own block), 3 (odd, division path) and
+    512 (more rows per block than a gather tile): write and gather."""
+    rng = np.random.default_rng(500 + bs)
+    nb = max(4, 600 // bs)
+    T = min(nb * bs, 333)
+    kv_c = synth.bf16_bits(rng.standard_normal((T, 512), dtype=np.float32))
+    k_pe = synth.bf16_bits(rng.standard_normal((T, 64), dtype=np.float32))
+    slots = synth.padded_slots(rng, nb * bs, T, 7)
+    want, flat = run_ds_write(orc, fmt, kv_c, k_pe, slots, nb, bs)
+    run_ds_gather(orc, fmt, want, flat, synth.per_token_gather("per-token", slots, nb, bs), nb, bs)
+    hi = bs * (nb // 3)                    # three requests always fit the cache
+    gc_ = synth.prefill_gather(rng, "prefill", 3, 1, hi, nb, bs, nb // 3)
+    run_ds_gather(orc, fmt, want, flat, gc_, nb, bs)
+
+
+@pytest.mark.parametrize("H,hs", [(1, 1024), (32, 16), (2, 48)])
+def test_perhead_extreme_heads(g, orc, H, hs):
+    """Largest head (1024 values), smallest head (16), one head, many heads,
+    and a head size that is not a power of two."""
+    rng = np.random.default_rng(H * 1000 + hs)
+    nb, bs, T = 12, 16, 150
+    key, value, slots = _kv_case(rng, T, H, hs, nb, bs, 4)
+    L = orc.kv_layout_split(bs, H, hs)
+    run_kv(orc, g, key, value, slots, nb, bs, L, None, synth.global_scale(key), synth.global_scale(value))
+
+
 # ---------------------------------------------------------------------------
 # per-head NVFP4 K/V
 # ---------------------------------------------------------------------------
