@@ -138,12 +138,7 @@ def nvfp4_kv_split_views(kv_cache, num_heads, head_size, layout=None):
     if layout is None:
         layout = nvfp4_kv_split_layout(bs, num_heads, head_size)
     base = kv_cache.as_strided((kv_cache.untyped_storage().nbytes() - kv_cache.storage_offset(),), (1,))
-    need = (nb - 1) * layout.block_stride + layout.side_stride + max(
-        layout.data_offset + (bs - 1) * layout.data_token_stride + (num_heads - 1) * layout.data_head_stride
-        + head_size // 2,
-        layout.scale_offset + (bs - 1) * layout.scale_token_stride + (num_heads - 1) * layout.scale_head_stride
-        + head_size // 16) if nb else 0
-    if need > base.numel():
+    if _layout_extent(layout, nb, bs, num_heads, head_size) > base.numel():
         raise ValueError("layout reaches past the cache allocation")
     data, scale = [], []
     for side in (0, 1):
@@ -200,6 +195,22 @@ def cache_write_fp8_ds_mla(kv_c, k_pe, kv_cache, slot_mapping, stream=None):
     _ds_write("gcache_cache_write_fp8_ds_mla", kv_c, k_pe, kv_cache, slot_mapping, stream)
 
 
+def _check_walk_args(block_table, workspace_starts, seq_starts, batch_size):
+    """Shared checks of the gather walk's metadata; returns the batch size.
+    The block table's row stride is also the bound the kernels apply to a
+    row's block index, so its rows must be contiguous."""
+    if block_table.dim() != 2 or not block_table.is_contiguous():
+        raise ValueError("block_table must be a contiguous int32 [batch, max_blocks] tensor")
+    if workspace_starts.dim() != 1 or not workspace_starts.is_contiguous() or \
+            (seq_starts is not None and (seq_starts.dim() != 1 or not seq_starts.is_contiguous())):
+        raise ValueError("workspace_starts / seq_starts must be contiguous int32 vectors")
+    B = workspace_starts.numel() if batch_size is None else int(batch_size)
+    if B > workspace_starts.numel() or (seq_starts is not None and B > seq_starts.numel()) \
+            or B > block_table.shape[0]:
+        raise ValueError("batch_size exceeds workspace_starts / seq_starts / block_table")
+    return B
+
+
 def _ds_gather(fn_name, src_cache, dst, block_table, workspace_starts, seq_starts, batch_size, stream):
     dev = _dev_tensor(src_cache, torch.uint8, "src_cache").device
     _dev_tensor(dst, torch.bfloat16, "dst", dev)
@@ -211,12 +222,7 @@ def _ds_gather(fn_name, src_cache, dst, block_table, workspace_starts, seq_start
         return                                   # no rows: nothing to do
     if dst.dim() != 2 or dst.stride(1) != 1 or dst.shape[1] < 576:
         raise ValueError("dst must be bf16 [total_tokens, >=576] with unit last stride")
-    if block_table.dim() != 2 or block_table.stride(1) != 1:
-        raise ValueError("block_table must be int32 [batch, max_blocks] with unit last stride")
-    B = workspace_starts.numel() if batch_size is None else int(batch_size)
-    if B > workspace_starts.numel() or (seq_starts is not None and B > seq_starts.numel()) \
-            or B > block_table.shape[0]:
-        raise ValueError("batch_size exceeds workspace_starts / seq_starts / block_table")
+    B = _check_walk_args(block_table, workspace_starts, seq_starts, batch_size)
     nb, bs, bstr, estr = _ds_cache_geometry(src_cache, "src_cache")
     with torch.cuda.device(dev):
         st = getattr(load(), fn_name)(_ptr(src_cache), _ptr(dst), dst.shape[0], dst.stride(0),
@@ -262,7 +268,21 @@ def _kv_geometry(kv_cache, num_heads, head_size, layout):
         if not kv_cache.is_contiguous():
             raise ValueError("the default split layout needs a contiguous kv_cache")
         layout = nvfp4_kv_split_layout(bs, num_heads, head_size)
+    avail = kv_cache.untyped_storage().nbytes() - kv_cache.storage_offset()
+    if _layout_extent(layout, nb, bs, num_heads, head_size) > avail:
+        raise ValueError("the layout addresses bytes past the kv_cache allocation")
     return nb, bs, layout
+
+
+def _layout_extent(layout, nb, bs, num_heads, head_size):
+    """One past the last cache byte the layout addresses for nb blocks."""
+    if nb == 0:
+        return 0
+    side = max(layout.data_offset + (bs - 1) * layout.data_token_stride
+               + (num_heads - 1) * layout.data_head_stride + head_size // 2,
+               layout.scale_offset + (bs - 1) * layout.scale_token_stride
+               + (num_heads - 1) * layout.scale_head_stride + head_size // 16)
+    return (nb - 1) * layout.block_stride + layout.side_stride + side
 
 
 def _scale(t, name, dev):
@@ -316,12 +336,10 @@ def gather_upconvert_nvfp4_kv(kv_cache, key_out, value_out, block_table, workspa
     if key_out.dim() != 3 or value_out.shape != key_out.shape or key_out.stride(2) != 1 \
             or value_out.stride(2) != 1:
         raise ValueError("key_out / value_out must be bf16 [total, H, hs] with unit last stride")
-    if block_table.dim() != 2 or block_table.stride(1) != 1:
-        raise ValueError("block_table must be int32 [batch, max_blocks] with unit last stride")
     total, H, hs = key_out.shape
     if total == 0:
         return
-    B = workspace_starts.numel() if batch_size is None else int(batch_size)
+    B = _check_walk_args(block_table, workspace_starts, seq_starts, batch_size)
     nb, bs, layout = _kv_geometry(kv_cache, H, hs, layout)
     with torch.cuda.device(dev):
         st = load().gcache_gather_upconvert_nvfp4_kv(
@@ -396,8 +414,8 @@ def convert_req_index_to_global_index(req_id, token_indices, block_table, block_
     _dev_tensor(block_table, torch.int32, "block_table", dev)
     if token_indices.dim() != 2 or token_indices.stride(1) != 1:
         raise ValueError("token_indices must be int32 [num_tokens, topk] with unit last stride")
-    if block_table.dim() != 2 or block_table.stride(1) != 1:
-        raise ValueError("block_table must be int32 [batch, max_blocks] with unit last stride")
+    if block_table.dim() != 2 or not block_table.is_contiguous():
+        raise ValueError("block_table must be a contiguous int32 [batch, max_blocks] tensor")
     if req_id.dim() != 1 or req_id.stride(0) != 1:
         raise ValueError("req_id must be a contiguous int32 vector")
     T, K = token_indices.shape

@@ -613,3 +613,27 @@ def test_side_stream_and_graph_replay(g, orc):
         torch.cuda.synchronize()
         assert_same(host(cache2).reshape(-1), want, f"graph replay {rep}: write")
         assert_same(host(dst2), rows, f"graph replay {rep}: gather")
+
+
+def test_binding_rejects_unsafe_arguments(g):
+    """Arguments the kernels could not bound are refused before any launch:
+    a block table whose rows are not contiguous, a batch larger than the
+    metadata, and a per-head layout that reaches past the cache tensor."""
+    cache = torch.zeros((4, 16, NV), dtype=torch.uint8, device="cuda")
+    dst = torch.zeros((8, 576), dtype=torch.bfloat16, device="cuda")
+    ws = torch.zeros(2, dtype=torch.int32, device="cuda")
+    wide = torch.zeros((2, 8), dtype=torch.int32, device="cuda")
+    with pytest.raises(ValueError):
+        g.cache_gather_upconvert_nvfp4_ds_mla(cache, dst, wide[:, :3], ws)
+    with pytest.raises(ValueError):
+        g.cache_gather_upconvert_nvfp4_ds_mla(cache, dst, wide, ws, batch_size=3)
+    H, hs, bs, nb = 2, 32, 4, 3
+    fd = hs // 2 + hs // 16
+    kv = torch.zeros((nb, 2, bs, H, fd), dtype=torch.uint8, device="cuda")
+    L = g.nvfp4_kv_split_layout(bs, H, hs)
+    L.block_stride += 64                        # the last block would run past the tensor
+    key = torch.zeros((5, H, hs), dtype=torch.bfloat16, device="cuda")
+    one = torch.ones(1, dtype=torch.float32, device="cuda")
+    with pytest.raises(ValueError):
+        g.reshape_and_cache_nvfp4(key, key, kv, torch.zeros(5, dtype=torch.int64, device="cuda"), one, one,
+                                  layout=L)
