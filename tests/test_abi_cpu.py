@@ -149,3 +149,17 @@ def test_perhead_argument_validation(lib):
     assert call(L=C.byref(bad)) == -3
     bad.data_head_stride = -64
     assert call(L=C.byref(bad)) == -2
+
+
+def test_binding_exposes_the_c_names(lib):
+    """Every device entry point (and the layout/size helpers) is reachable
+    from Python under its C name; the host-only chunk planner and the HND
+    layout are reached through context_chunks and
+    nvfp4_kv_split_layout(hnd=True), gcache_status_string through the
+    exception text."""
+    import gather_concat_cache_amd as g
+    wrapped_elsewhere = {"gcache_status_string", "gcache_context_chunk_plan", "gcache_context_chunk",
+                         "gcache_nvfp4_kv_split_layout_hnd"}
+    for n in declared_functions():
+        if n not in wrapped_elsewhere:
+            assert callable(getattr(g, n, None)), f"{n} has no Python counterpart"
