@@ -62,11 +62,12 @@ def build(verbose: bool = False) -> str:
 
 
 def source_digest() -> str:
-    """sha256 of every source and header the library is built from."""
+    """sha256 of every source and header the library is built from (the
+    kernels, their headers and the C ABI header)."""
     import hashlib
     h = hashlib.sha256()
-    for f in SOURCES + HEADERS:
-        with open(os.path.join(CSRC, f), "rb") as fh:
+    for path in [os.path.join(CSRC, f) for f in SOURCES + HEADERS] + [os.path.join(ROOT, "include", "gcache.h")]:
+        with open(path, "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
