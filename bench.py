@@ -166,7 +166,8 @@ def main():
     if args.extras_only:
         ops[0][3]()                                  # the nvfp4 pre-fill the extras read
         torch.cuda.synchronize()
-        print(json.dumps({"extras": measure_extras(torch, gc, g3, args.steps, dev_arr, d["cache3"])}), flush=True)
+        print(json.dumps({"extras": measure_extras(torch, gc, g3, args.steps, dev_arr, d["cache3"],
+                                                   (w5, g5, d))}), flush=True)
         return
     if args.only:
         keep = set(args.only.split(","))
@@ -205,7 +206,8 @@ def main():
                          "GB_per_s": round(nbytes / (ms * 1e6), 1),
                          "frac_of_hbm_peak": round(nbytes / (ms * 1e6) / HBM_PEAK_GBS, 4)}
 
-    extras = None if args.no_extras else measure_extras(torch, gc, g3, args.steps, dev_arr, d["cache3"])
+    extras = None if args.no_extras else measure_extras(torch, gc, g3, args.steps, dev_arr, d["cache3"],
+                                                        (w5, g5, d))
 
     if args.copy_calibration:
         # a plain elementwise kernel that reads and writes exactly n bytes each
@@ -254,7 +256,7 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def measure_extras(torch, gc, g3, steps, dev_arr, cache3):
+def measure_extras(torch, gc, g3, steps, dev_arr, cache3, perhead):
     """Outside the timed step: (1) the BF16 comparator gather (same walk,
     1152-byte bf16 entries copied) over the nvfp4 prefill gather's requests
     and cache geometry -- what a walk-driven gather of full rows reaches on
@@ -349,6 +351,39 @@ def measure_extras(torch, gc, g3, steps, dev_arr, cache3):
         "GB_per_s": round(nbytes / (ms * 1e6), 1), "frac_of_hbm_peak": round(nbytes / (ms * 1e6) / HBM_PEAK_GBS, 4),
         "workload": f"{idx.shape[0]} token rows x top-{idx.shape[1]} positions over {sbt.shape[0]} requests "
                     "(4 B read + 4 B written per index; block-table reads not counted)"}
+
+    # (4) the per-head workload with reading B of its layout: every
+    # (token, head) row of the cache is [hs/2 data bytes | hs/16 scale bytes]
+    w5, g5, d = perhead
+    H, hs = w5.key.shape[1], w5.key.shape[2]
+    fd = hs // 2 + hs // 16
+    bs = w5.block_size
+    Lb = gc.NvFp4KvLayout(data_offset=0, data_token_stride=H * fd, data_head_stride=fd, scale_offset=hs // 2,
+                          scale_token_stride=H * fd, scale_head_stride=fd, side_stride=bs * H * fd,
+                          block_stride=2 * bs * H * fd)
+    cache_b = torch.zeros((w5.num_blocks, 2, bs, H, fd), dtype=torch.uint8, device="cuda")
+    for name, fn, nbytes, units in (
+            ("perhead_write_interleaved_rows",
+             lambda: gc.reshape_and_cache_nvfp4(d["k5"], d["v5"], cache_b, d["sl5"], d["ks5"], d["vs5"], layout=Lb),
+             kv_write_bytes(w5), w5.slot_mapping.shape[0]),
+            ("perhead_gather_interleaved_rows",
+             lambda: gc.gather_upconvert_nvfp4_kv(cache_b, d["ko5"], d["vo5"], d["bt5"], d["ws5"], d["ks5"],
+                                                  d["vs5"], seq_starts=d["ss5"], layout=Lb),
+             kv_gather_bytes(g5, H, hs), g5.total_tokens)):
+        fn()
+        ev = [mk() for _ in range(steps)]
+        for a, b in ev:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+        out[name] = {"ms": round(ms, 5), "bytes": nbytes, "units": units,
+                     "GB_per_s": round(nbytes / (ms * 1e6), 1),
+                     "frac_of_hbm_peak": round(nbytes / (ms * 1e6) / HBM_PEAK_GBS, 4),
+                     "workload": f"the per-head workload ({units} tokens / rows x {H} heads x {hs}) with each "
+                                 f"(token, head) cache row laid out as [{hs // 2} data | {hs // 16} scale] bytes"}
+    del cache_b
     return out
 
 
