@@ -256,38 +256,52 @@ def main():
     print(json.dumps(out), flush=True)
 
 
+def device_ms(torch, fn, steps, spin_cycles=300_000):
+    """Mean device time of fn() over `steps` launches.  Each launch is queued
+    behind a short spin kernel, so the HIP events around it (on the launch
+    stream) see only GPU work: the host's per-call overhead cannot leave the
+    GPU idle between the first event and the kernel."""
+    fn()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in ev:
+        torch.cuda._sleep(spin_cycles)
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+
+def _extra(ms, nbytes, units, workload, **more):
+    return {"ms": round(ms, 5), "bytes": nbytes, "units": units, **more,
+            "GB_per_s": round(nbytes / (ms * 1e6), 1),
+            "frac_of_hbm_peak": round(nbytes / (ms * 1e6) / HBM_PEAK_GBS, 4), "workload": workload}
+
+
 def measure_extras(torch, gc, g3, steps, dev_arr, cache3, perhead):
-    """Outside the timed step: (1) the BF16 comparator gather (same walk,
-    1152-byte bf16 entries copied) over the nvfp4 prefill gather's requests
-    and cache geometry -- what a walk-driven gather of full rows reaches on
-    this device; (2) the chunked-context driver gathering every request's
-    whole nvfp4 context (lengths of the prefill gather's requests, from
-    position 0) through a 65536-row workspace.  HIP events on the launch
-    stream, mean over `steps`."""
+    """Outside the timed step, device times (see device_ms) of:
+    (1) the BF16 comparator gather (same walk, 1152-byte bf16 entries copied)
+        over the nvfp4 prefill gather's requests and cache geometry -- what a
+        walk-driven gather of full rows reaches on this device;
+    (2) the chunked-context driver gathering every request's whole nvfp4
+        context (the prefill requests' lengths, from position 0) through a
+        65536-row workspace, and the same pass's wall time on an idle GPU;
+    (3) the sparse index conversion, 4096 rows x top-2048;
+    (4) the per-head workload under the split layout and under reading B
+        (interleaved [data | scale] rows)."""
     import synth
+    out = {}
     nb, bs = g3.num_blocks, g3.block_size
     cache = torch.from_numpy(synth.normal_bf16_rows(1013, 0, nb * bs, 576).view(np.int16)) \
         .view(torch.bfloat16).reshape(nb, bs, 576).cuda()
     dst = torch.empty((g3.total_tokens, 576), dtype=torch.bfloat16, device="cuda")
     bt, ws, ss = dev_arr(g3.block_table), dev_arr(g3.workspace_starts), dev_arr(g3.seq_starts)
-    run = lambda: gc.cache_gather_bf16(cache, dst, bt, ws, ss)
-    for _ in range(3):
-        run()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for a, b in ev:
-        a.record()
-        run()
-        b.record()
-    torch.cuda.synchronize()
-    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
-    nbytes = g3.total_tokens * 2 * 1152
+    ms = device_ms(torch, lambda: gc.cache_gather_bf16(cache, dst, bt, ws, ss), steps)
+    out["bf16_gather_comparator"] = _extra(
+        ms, g3.total_tokens * 2 * 1152, g3.total_tokens,
+        f"{g3.total_tokens} rows of the nvfp4 prefill gather over a bf16 cache {nb} x {bs} x 1152 B "
+        "(1152 B read + 1152 B written per row)", rows_per_s=round(g3.total_tokens / (ms * 1e-3), 1))
     del cache, dst
-    out = {"bf16_gather_comparator": {
-        "ms": round(ms, 5), "bytes": nbytes, "units": g3.total_tokens,
-        "GB_per_s": round(nbytes / (ms * 1e6), 1), "frac_of_hbm_peak": round(nbytes / (ms * 1e6) / HBM_PEAK_GBS, 4),
-        "rows_per_s": round(g3.total_tokens / (ms * 1e-3), 1),
-        "workload": f"{g3.total_tokens} rows of the nvfp4 prefill gather over a bf16 cache "
-                    f"{nb} x {bs} x 1152 B (1152 B read + 1152 B written per row)"}}
 
     lens = np.asarray(g3.lengths, np.int32)
     ws_rows = 65536
@@ -295,95 +309,63 @@ def measure_extras(torch, gc, g3, steps, dev_arr, cache3, perhead):
     _, plan = gc.context_chunks(lens, ws_rows, bs)
     rows = int(sum(t for _, _, t in plan))
 
-    # Device time: the chunk gathers are enqueued behind a short spin kernel,
-    # so they run back to back and the events around them see only GPU work
-    # (metadata upload included).  Wall time: the same pass enqueued on an
-    # idle GPU, so the host's per-chunk call overhead shows as gaps.
     def chunked():
         for _ in gc.gather_context_chunked(gc.cache_gather_upconvert_nvfp4_ds_mla, cache3, workspace, bt, lens):
             pass
-    chunked()
-    mk = lambda: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-    dev_t, wall_t = [], []
-    for i in range(steps):
-        a, b = mk()
-        torch.cuda._sleep(2_000_000)
-        a.record()
-        chunked()
-        b.record()
+    busy = device_ms(torch, chunked, steps, spin_cycles=2_000_000)
+    wall_t = []
+    for _ in range(steps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
-        dev_t.append(a.elapsed_time(b))
-        a, b = mk()
         a.record()
         chunked()
         b.record()
         torch.cuda.synchronize()
         wall_t.append(a.elapsed_time(b))
-    busy, wall = float(np.mean(dev_t)), float(np.mean(wall_t))
+    wall = float(np.mean(wall_t))
     nbytes = rows * (NV + 1152)
-    out["chunked_context_nvfp4_gather"] = {
-        "ms": round(busy, 5), "wall_ms": round(wall, 5), "bytes": nbytes, "units": rows, "chunks": len(plan),
-        "GB_per_s": round(nbytes / (busy * 1e6), 1), "frac_of_hbm_peak": round(nbytes / (busy * 1e6) / HBM_PEAK_GBS, 4),
-        "wall_GB_per_s": round(nbytes / (wall * 1e6), 1),
-        "workload": f"whole contexts of the {lens.shape[0]} prefill requests ({rows} positions) gathered in "
-                    f"{len(plan)} chunks through a {ws_rows}-row workspace; ms = device time of the pass "
-                    "(launches queued behind a spin kernel), wall_ms = the pass on an idle GPU, host call "
-                    "overhead included"}
+    out["chunked_context_nvfp4_gather"] = _extra(
+        busy, nbytes, rows,
+        f"whole contexts of the {lens.shape[0]} prefill requests ({rows} positions) gathered in {len(plan)} "
+        f"chunks through a {ws_rows}-row workspace; ms = device time of the pass (metadata upload included), "
+        "wall_ms = the pass on an idle GPU, host call overhead included",
+        chunks=len(plan), wall_ms=round(wall, 5), wall_GB_per_s=round(nbytes / (wall * 1e6), 1))
     del workspace
 
-    # (3) sparse index conversion: 4096 token rows x top-2048 positions
     req, idx, sbt, sbs, snb = synth.sparse_index_case()
     req_d, idx_d, sbt_d = dev_arr(req), dev_arr(idx), dev_arr(sbt)
     sout = torch.empty_like(idx_d)
-    conv = lambda: gc.convert_req_index_to_global_index(req_d, idx_d, sbt_d, sbs, snb, out=sout)
-    for _ in range(3):
-        conv()
-    ev = [mk() for _ in range(steps)]
-    for a, b in ev:
-        a.record()
-        conv()
-        b.record()
-    torch.cuda.synchronize()
-    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
-    nbytes = idx.size * 8 + req.size * 4
-    out["sparse_index_conversion"] = {
-        "ms": round(ms, 5), "bytes": nbytes, "units": int(idx.size),
-        "GB_per_s": round(nbytes / (ms * 1e6), 1), "frac_of_hbm_peak": round(nbytes / (ms * 1e6) / HBM_PEAK_GBS, 4),
-        "workload": f"{idx.shape[0]} token rows x top-{idx.shape[1]} positions over {sbt.shape[0]} requests "
-                    "(4 B read + 4 B written per index; block-table reads not counted)"}
+    ms = device_ms(torch, lambda: gc.convert_req_index_to_global_index(req_d, idx_d, sbt_d, sbs, snb, out=sout),
+                   steps)
+    out["sparse_index_conversion"] = _extra(
+        ms, idx.size * 8 + req.size * 4, int(idx.size),
+        f"{idx.shape[0]} token rows x top-{idx.shape[1]} positions over {sbt.shape[0]} requests "
+        "(4 B read + 4 B written per index; block-table reads not counted)")
 
-    # (4) the per-head workload with reading B of its layout: every
-    # (token, head) row of the cache is [hs/2 data bytes | hs/16 scale bytes]
     w5, g5, d = perhead
     H, hs = w5.key.shape[1], w5.key.shape[2]
     fd = hs // 2 + hs // 16
-    bs = w5.block_size
-    Lb = gc.NvFp4KvLayout(data_offset=0, data_token_stride=H * fd, data_head_stride=fd, scale_offset=hs // 2,
-                          scale_token_stride=H * fd, scale_head_stride=fd, side_stride=bs * H * fd,
-                          block_stride=2 * bs * H * fd)
-    cache_b = torch.zeros((w5.num_blocks, 2, bs, H, fd), dtype=torch.uint8, device="cuda")
-    for name, fn, nbytes, units in (
-            ("perhead_write_interleaved_rows",
-             lambda: gc.reshape_and_cache_nvfp4(d["k5"], d["v5"], cache_b, d["sl5"], d["ks5"], d["vs5"], layout=Lb),
-             kv_write_bytes(w5), w5.slot_mapping.shape[0]),
-            ("perhead_gather_interleaved_rows",
-             lambda: gc.gather_upconvert_nvfp4_kv(cache_b, d["ko5"], d["vo5"], d["bt5"], d["ws5"], d["ks5"],
-                                                  d["vs5"], seq_starts=d["ss5"], layout=Lb),
-             kv_gather_bytes(g5, H, hs), g5.total_tokens)):
-        fn()
-        ev = [mk() for _ in range(steps)]
-        for a, b in ev:
-            a.record()
-            fn()
-            b.record()
-        torch.cuda.synchronize()
-        ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
-        out[name] = {"ms": round(ms, 5), "bytes": nbytes, "units": units,
-                     "GB_per_s": round(nbytes / (ms * 1e6), 1),
-                     "frac_of_hbm_peak": round(nbytes / (ms * 1e6) / HBM_PEAK_GBS, 4),
-                     "workload": f"the per-head workload ({units} tokens / rows x {H} heads x {hs}) with each "
-                                 f"(token, head) cache row laid out as [{hs // 2} data | {hs // 16} scale] bytes"}
-    del cache_b
+    bs5 = w5.block_size
+    layouts = {
+        "split_rows": gc.nvfp4_kv_split_layout(bs5, H, hs),
+        "interleaved_rows": gc.NvFp4KvLayout(
+            data_offset=0, data_token_stride=H * fd, data_head_stride=fd, scale_offset=hs // 2,
+            scale_token_stride=H * fd, scale_head_stride=fd, side_stride=bs5 * H * fd,
+            block_stride=2 * bs5 * H * fd)}
+    cache5 = torch.zeros((w5.num_blocks, 2, bs5, H, fd), dtype=torch.uint8, device="cuda")
+    for lname, L in layouts.items():
+        what = ("the default split layout" if lname == "split_rows" else
+                f"each (token, head) cache row laid out as [{hs // 2} data | {hs // 16} scale] bytes")
+        ms = device_ms(torch, lambda: gc.reshape_and_cache_nvfp4(d["k5"], d["v5"], cache5, d["sl5"], d["ks5"],
+                                                                 d["vs5"], layout=L), steps)
+        out[f"perhead_write_{lname}"] = _extra(ms, kv_write_bytes(w5), w5.slot_mapping.shape[0],
+                                               f"the per-head write workload, {what}")
+        ms = device_ms(torch, lambda: gc.gather_upconvert_nvfp4_kv(cache5, d["ko5"], d["vo5"], d["bt5"], d["ws5"],
+                                                                   d["ks5"], d["vs5"], seq_starts=d["ss5"],
+                                                                   layout=L), steps)
+        out[f"perhead_gather_{lname}"] = _extra(ms, kv_gather_bytes(g5, H, hs), g5.total_tokens,
+                                                f"the per-head gather workload, {what}")
+    del cache5
     return out
 
 

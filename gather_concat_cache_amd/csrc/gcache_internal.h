@@ -54,6 +54,7 @@ struct KvWriteParams {
     BlockDiv div;
     KvLayout L;
     const float* gscale[2];      // k_scale, v_scale (device scalars)
+    int32_t span;                // > 0: staged kernels, contiguous (token, side) run bytes
 };
 
 struct KvGatherParams {
@@ -72,6 +73,7 @@ struct KvGatherParams {
     BlockDiv div;
     KvLayout L;
     const float* gscale[2];
+    int32_t span;                // > 0: staged kernels, contiguous (token, side) run bytes
 };
 
 struct SparseIndexParams {
@@ -95,6 +97,7 @@ hipError_t launch_gather_nvfp4_ds_mla(const DsMlaGatherParams& p, hipStream_t s)
 hipError_t launch_gather_fp8_ds_mla(const DsMlaGatherParams& p, hipStream_t s);
 hipError_t launch_gather_bf16(const DsMlaGatherParams& p, hipStream_t s);
 hipError_t launch_reshape_and_cache_nvfp4(const KvWriteParams& p, hipStream_t s);
+int32_t staged_span(const KvLayout& L, int32_t num_heads, int32_t head_size);
 hipError_t launch_gather_nvfp4_kv(const KvGatherParams& p, hipStream_t s);
 hipError_t launch_convert_req_index(const SparseIndexParams& p, hipStream_t s);
 

@@ -468,18 +468,24 @@ def test_perhead_config5(g, orc):
            w.k_scale, w.v_scale)
 
 
-@pytest.mark.parametrize("variant", ["interleaved", "hnd", "hnd-split", "odd-head-size", "strided-input"])
+@pytest.mark.parametrize("variant", ["interleaved", "interleaved-3heads", "hnd", "hnd-split", "odd-head-size",
+                                     "strided-input"])
 def test_perhead_layouts(g, orc, variant):
-    seed = {"interleaved": 41, "hnd": 42, "hnd-split": 45, "odd-head-size": 43, "strided-input": 44}[variant]
+    """Layouts: interleaved [data | scales] rows (4 heads: 16-byte aligned
+    token runs, the staged kernels; 3 heads: 216-byte runs, the direct
+    kernels), HND orders, a head size of 80, strided inputs."""
+    seed = {"interleaved": 41, "interleaved-3heads": 47, "hnd": 42, "hnd-split": 45, "odd-head-size": 43,
+            "strided-input": 44}[variant]
     rng = np.random.default_rng(seed)
     # head size 80: 5 scale blocks and 10 chunks per head (the non-power-of-two paths)
     # interleaved [data | scales] rows keep 8-byte data alignment at head size 128 (72-byte rows)
-    H, hs, nb, bs = {"odd-head-size": (3, 80, 20, 16), "interleaved": (4, 128, 16, 16)}.get(variant, (4, 64, 16, 16))
+    H, hs, nb, bs = {"odd-head-size": (3, 80, 20, 16), "interleaved": (4, 128, 16, 16),
+                     "interleaved-3heads": (3, 128, 16, 16)}.get(variant, (4, 64, 16, 16))
     T = 157
     key, value, slots = _kv_case(rng, T, H, hs, nb, bs, 9)
     ks, vs = synth.global_scale(key), synth.global_scale(value)
     fd = hs // 2 + hs // 16
-    if variant == "interleaved":        # each (token, head) row is [data | scales]
+    if variant.startswith("interleaved"):   # each (token, head) row is [data | scales]
         kw = dict(data_offset=0, data_token_stride=H * fd, data_head_stride=fd, scale_offset=hs // 2,
                   scale_token_stride=H * fd, scale_head_stride=fd, side_stride=bs * H * fd,
                   block_stride=2 * bs * H * fd)
