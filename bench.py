@@ -412,9 +412,9 @@ KERNEL_OPS = {
     "gcache::k_write_nvfp4_ds_mla": "nvfp4_ds_mla_write",
     "gcache::k_write_fp8_ds_mla": "fp8_ds_mla_write",
     "void gcache::k_gather_ds_mla<true>": "nvfp4_ds_mla_gather",
-    "gcache::k_reshape_and_cache_nvfp4": "nvfp4_kv_write",
+    "void gcache::k_reshape_and_cache_nvfp4<false>": "nvfp4_kv_write",
     "void gcache::k_gather_ds_mla<false>": "fp8_ds_mla_gather",
-    "gcache::k_gather_nvfp4_kv": "nvfp4_kv_gather",
+    "void gcache::k_gather_nvfp4_kv<false>": "nvfp4_kv_gather",
 }
 CALIBRATION_KERNEL = "CUDAFunctorOnSelf_add"
 
@@ -505,7 +505,7 @@ def write_stats(prof_dir, bench_json, extras=False):
     flags = "--extras-only" if extras else "--no-cpu-baseline --no-extras"
     cmd = ("rocprofv3 --kernel-trace --stats -f csv -d $R/" + os.path.relpath(prof_dir, ROOT) +
            f" -o bench -- python3 $R/bench.py --steps 20 --warmup 3 {flags}")
-    title = ("the bench extras (BF16 comparator, chunked context, sparse index conversion)" if extras
+    title = ("the bench extras (BF16 comparator, chunked context, sparse index conversion, per-head layouts)" if extras
              else "all six kernels, prefill-context pass workload")
     what = ("20 timed repetitions of each extra after one nvfp4 pre-fill write. The chunked-context pass "
             "launches the nvfp4 gather once per chunk (8 chunks), so its calls share that kernel's name; "
