@@ -288,7 +288,12 @@ def measure_extras(torch, gc, g3, steps, dev_arr, cache3, perhead):
         65536-row workspace, and the same pass's wall time on an idle GPU;
     (3) the sparse index conversion, 4096 rows x top-2048;
     (4) the per-head workload under the split layout and under reading B
-        (interleaved [data | scale] rows)."""
+        (interleaved [data | scale] rows);
+    (5) the decode-batch nvfp4 write (4096 tokens, lognormal magnitudes with
+        outliers, 2% padding) and the per-head pair, warm (back to back) and
+        cold (each launch after a 2 GiB write that evicts L2 and the MALL).
+        These launches move a few to a few tens of MB: launch and ramp, not
+        HBM bandwidth, set their time."""
     import synth
     out = {}
     nb, bs = g3.num_blocks, g3.block_size
@@ -366,6 +371,29 @@ def measure_extras(torch, gc, g3, steps, dev_arr, cache3, perhead):
         out[f"perhead_gather_{lname}"] = _extra(ms, kv_gather_bytes(g5, H, hs), g5.total_tokens,
                                                 f"the per-head gather workload, {what}")
     del cache5
+
+    w2 = synth.config2()
+    kv2, pe2 = (torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+                for a in (w2.kv_c, w2.k_pe))
+    sl2 = dev_arr(w2.slot_mapping)
+    cache2 = torch.zeros((w2.num_blocks, w2.block_size, NV), dtype=torch.uint8, device="cuda")
+    small = [("decode_batch_nvfp4_write", ds_write_bytes(w2, NV), w2.num_tokens,
+              lambda: gc.cache_write_nvfp4_ds_mla(kv2, pe2, cache2, sl2),
+              f"{w2.num_tokens} decode tokens (lognormal magnitudes, 1% x50 outliers, "
+              f"{int((w2.slot_mapping < 0).sum())} padding slots) into {w2.num_blocks} x {w2.block_size} x 352 B"),
+             ("perhead_write_cold_warm", kv_write_bytes(w5), w5.slot_mapping.shape[0],
+              lambda: gc.reshape_and_cache_nvfp4(d["k5"], d["v5"], d["cache5"], d["sl5"], d["ks5"], d["vs5"]),
+              "the per-head write workload, default split layout"),
+             ("perhead_gather_cold_warm", kv_gather_bytes(g5, H, hs), g5.total_tokens,
+              lambda: gc.gather_upconvert_nvfp4_kv(d["cache5"], d["ko5"], d["vo5"], d["bt5"], d["ws5"], d["ks5"],
+                                                   d["vs5"], seq_starts=d["ss5"]),
+              "the per-head gather workload, default split layout")]
+    cold = measure_cold(torch, [(n, b, u, fn) for n, b, u, fn, _ in small])
+    for name, nbytes, units, fn, what in small:
+        warm = device_ms(torch, fn, steps)
+        out[name] = _extra(warm, nbytes, units, what + "; ms = warm (back to back), cold_ms = after evicting "
+                           "L2 and the MALL", cold_ms=cold[name]["ms"], cold_GB_per_s=cold[name]["GB_per_s"])
+    del cache2
     return out
 
 
