@@ -461,11 +461,23 @@ def run_kv(orc, g, key, value, slots, nb, bs, L_orc, L_gpu, ks, vs, key_dev=None
     assert_same(host(vo.contiguous()), ov, "per-head gather V")
 
 
-def test_perhead_config5(g, orc):
+@pytest.mark.parametrize("layout", ["split", "interleaved-rows"])
+def test_perhead_config5(g, orc, layout):
+    """The per-head workload at full size (8192 tokens, 8 heads of 128,
+    4096 blocks of 16), every byte and output bit: the default split layout
+    (direct kernels) and [data | scale] rows per (token, head) (576-byte
+    runs per token and side, the staged kernels), as the bench times them."""
     w, _ = synth.config5()
-    L_orc = orc.kv_layout_split(w.block_size, 8, 128)
-    run_kv(orc, g, w.key, w.value, w.slot_mapping, w.num_blocks, w.block_size, L_orc, None,
-           w.k_scale, w.v_scale)
+    H, hs, bs = 8, 128, w.block_size
+    if layout == "split":
+        L_orc, L_gpu = orc.kv_layout_split(bs, H, hs), None
+    else:
+        fd = hs // 2 + hs // 16
+        kw = dict(data_offset=0, data_token_stride=H * fd, data_head_stride=fd, scale_offset=hs // 2,
+                  scale_token_stride=H * fd, scale_head_stride=fd, side_stride=bs * H * fd,
+                  block_stride=2 * bs * H * fd)
+        L_orc, L_gpu = orc.KvLayout(**kw), g.NvFp4KvLayout(**kw)
+    run_kv(orc, g, w.key, w.value, w.slot_mapping, w.num_blocks, bs, L_orc, L_gpu, w.k_scale, w.v_scale)
 
 
 @pytest.mark.parametrize("variant", ["interleaved", "interleaved-3heads", "hnd", "hnd-split", "odd-head-size",
