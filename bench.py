@@ -208,6 +208,10 @@ def main():
 
     extras = None if args.no_extras else measure_extras(torch, gc, g3, args.steps, dev_arr, d["cache3"],
                                                         (w5, g5, d))
+    if extras is not None:
+        mix = {"nvfp4_ds_mla_write": (w3.num_tokens, 1152, NV), "fp8_ds_mla_write": (w4.num_tokens, 1152, F8),
+               "nvfp4_ds_mla_gather": (g3.total_tokens, NV, 1152), "fp8_ds_mla_gather": (g4.total_tokens, F8, 1152)}
+        extras["same_mix_ceilings"] = measure_ceilings(torch, [o for o in ops if o[0] in mix], mix)
 
     if args.copy_calibration:
         # a plain elementwise kernel that reads and writes exactly n bytes each
@@ -394,6 +398,42 @@ def measure_extras(torch, gc, g3, steps, dev_arr, cache3, perhead):
         out[name] = _extra(warm, nbytes, units, what + "; ms = warm (back to back), cold_ms = after evicting "
                            "L2 and the MALL", cold_ms=cold[name]["ms"], cold_GB_per_s=cold[name]["GB_per_s"])
     del cache2
+    return out
+
+
+def measure_ceilings(torch, ops, mix, reps=5):
+    """For each DS-MLA op: the same-mix row copy of libgcache_bench.so (rows
+    of the op's read bytes in, its write bytes out, contiguous, 16-row LDS
+    tiles, no walk and no conversion) and the op itself, both cold (each
+    launch after a 2 GiB write that evicts L2 and the MALL), so the op can be
+    stated as a fraction of what a plain stream with its byte pattern reaches
+    on this device."""
+    import ctypes
+    from gather_concat_cache_amd import build
+    lib = ctypes.CDLL(build.BENCH_LIB)
+    fn = lib.gcache_bench_copy_mix
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                   ctypes.c_void_p]
+    fn.restype = ctypes.c_int
+    op_cold = measure_cold(torch, ops, reps)
+    out = {}
+    for name, nbytes, _, _ in ops:
+        rows, rb, wb = mix[name]
+        src = torch.empty(rows * rb, dtype=torch.uint8, device="cuda").fill_(0x3C)
+        dst = torch.empty(rows * wb, dtype=torch.uint8, device="cuda")
+        stream = torch.cuda.current_stream().cuda_stream
+
+        def copy():
+            rc = fn(src.data_ptr(), dst.data_ptr(), rows, rb, wb, stream)
+            if rc != 0:
+                raise RuntimeError(f"gcache_bench_copy_mix returned {rc}")
+        cbytes = rows * (rb + wb)
+        ceil = measure_cold(torch, [(name, cbytes, rows, copy)], reps)[name]
+        op_gbs = op_cold[name]["GB_per_s"]
+        out[name] = {"rows": rows, "read_bytes": rb, "write_bytes": wb, "ceiling_ms": ceil["ms"],
+                     "ceiling_GB_per_s": ceil["GB_per_s"], "op_cold_ms": op_cold[name]["ms"],
+                     "op_cold_GB_per_s": op_gbs, "frac_of_ceiling": round(op_gbs / ceil["GB_per_s"], 4)}
+        del src, dst
     return out
 
 

@@ -21,6 +21,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libgcache.so")
 SOURCES = ["ds_mla_kernels.hip", "nvfp4_kv_kernels.hip", "sparse_index.hip", "gcache_abi.hip"]
+# measurement helper beside the library (include/gcache_bench.h), loaded by bench.py only
+BENCH_LIB = os.path.join(PKG, "libgcache_bench.so")
+BENCH_SOURCES = ["bench_ceiling.hip"]
 HEADERS = ["gcache_device.h", "gcache_internal.h"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
@@ -45,19 +48,26 @@ def _compile(src, obj, verbose):
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source for gfx950 and link libgcache.so."""
-    objdir = os.path.join(ROOT, "_build", "gcache")
-    os.makedirs(objdir, exist_ok=True)
-    objs = [os.path.join(objdir, s.replace(".hip", ".o")) for s in SOURCES]
-    with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        list(ex.map(lambda so: _compile(*so, verbose), zip(SOURCES, objs)))
-    tmp = LIB + ".tmp"
+def _link(lib, objs, verbose):
+    tmp = lib + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source for gfx950 and link libgcache.so (and the
+    measurement helper libgcache_bench.so)."""
+    objdir = os.path.join(ROOT, "_build", "gcache")
+    os.makedirs(objdir, exist_ok=True)
+    srcs = SOURCES + BENCH_SOURCES
+    objs = [os.path.join(objdir, s.replace(".hip", ".o")) for s in srcs]
+    with cf.ThreadPoolExecutor(max_workers=len(srcs)) as ex:
+        list(ex.map(lambda so: _compile(*so, verbose), zip(srcs, objs)))
+    _link(LIB, objs[:len(SOURCES)], verbose)
+    _link(BENCH_LIB, objs[len(SOURCES):], verbose)
     return LIB
 
 

@@ -163,3 +163,24 @@ def test_binding_exposes_the_c_names(lib):
     for n in declared_functions():
         if n not in wrapped_elsewhere:
             assert callable(getattr(g, n, None)), f"{n} has no Python counterpart"
+
+
+def test_bench_helper_library():
+    """libgcache_bench.so (the same-mix copy bench.py measures as a ceiling)
+    loads, exports what include/gcache_bench.h declares, and rejects bad
+    arguments before touching the device."""
+    from gather_concat_cache_amd import build
+    if not os.path.exists(build.BENCH_LIB):
+        build.build()
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "gcache_bench.h")).read(), flags=re.S)
+    assert sorted(set(re.findall(r"\b(gcache_[a-z0-9_]+)\s*\(", text))) == ["gcache_bench_copy_mix"]
+    blib = C.CDLL(build.BENCH_LIB)
+    f = blib.gcache_bench_copy_mix
+    f.argtypes = [C.c_void_p, C.c_void_p, C.c_int64, C.c_int32, C.c_int32, C.c_void_p]
+    f.restype = C.c_int
+    assert f(None, None, 0, 352, 1152, None) == 0           # empty: no-op
+    assert f(None, A16, 10, 352, 1152, None) == -1
+    assert f(A16, A16, 10, 350, 1152, None) == -2
+    assert f(A16, A16, 10, 352, 1168, None) == -2
+    assert f(A16, A16, -1, 352, 1152, None) == -2
+    assert f(A16 + 8, A16, 10, 352, 1152, None) == -3
