@@ -9,6 +9,12 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 GOLDEN = os.path.join(ROOT, "tests", "golden")
 
+# GCACHE_ORACLE_LIB names another build of the oracle's sources (the
+# sanitized build of test_oracle_sanitized.py) for every test in this run.
+if os.environ.get("GCACHE_ORACLE_LIB"):
+    import oracle
+    oracle._lib = oracle.lib(os.environ["GCACHE_ORACLE_LIB"])
+
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an AMD Instinct MI355X (gfx950) GPU")
