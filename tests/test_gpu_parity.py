@@ -633,6 +633,92 @@ def test_side_stream_and_graph_replay(g, orc):
         assert_same(host(dst2), rows, f"graph replay {rep}: gather")
 
 
+@pytest.mark.parametrize("fmt", ["nvfp4", "fp8"])
+def test_cache_offsets_beyond_4gib(g, orc, fmt):
+    """A cache of more than 5 GiB: tokens written into its last four blocks
+    (entry offsets above 2^32, so the kernels' 64-bit address arithmetic is
+    exercised) and gathered back from there by two requests, against the
+    oracle on a compact cache of just those four blocks; blocks below stay
+    untouched."""
+    eb, gwrite, ggather = _ds_pair(fmt)
+    owrite, ogather = _orc_ds(orc, fmt)
+    bs = 64
+    nb = (5 << 30) // (bs * eb) + 1
+    hi = nb - 4
+    assert hi * bs * eb > (1 << 32)
+    rng = np.random.default_rng(71)
+    T = 4 * bs
+    kv_c = synth.bf16_bits(rng.standard_normal((T, 512), dtype=np.float32))
+    k_pe = synth.bf16_bits(rng.standard_normal((T, 64), dtype=np.float32))
+    local = rng.permutation(T).astype(np.int64)
+    local[::17] = -1
+    compact = np.full(4 * bs * eb, 0xA5, np.uint8)
+    owrite(kv_c, k_pe, compact, local, 4, bs)
+    slots = np.where(local >= 0, local + hi * bs, -1)
+    print(f"cache beyond 4 GiB: {fmt}, {nb} blocks, {nb * bs * eb / 2**30:.2f} GiB", flush=True)
+    cache = torch.full((nb, bs, eb), 0xA5, dtype=torch.uint8, device="cuda")
+    gwrite(dev(kv_c), dev(k_pe), cache, dev(slots))
+    torch.cuda.synchronize()
+    assert_same(host(cache[hi:]).reshape(-1), compact, f"{fmt} entries above 4 GiB")
+    assert_same(host(cache[hi - 2:hi]).reshape(-1), np.full(2 * bs * eb, 0xA5, np.uint8), "blocks below")
+
+    bt_local = np.array([[2, 0, 3, 1], [1, 3, -1, -1]], np.int32)
+    ss = np.array([3, 0], np.int32)
+    rows = np.array([4 * bs - 5, 2 * bs], np.int64) - ss
+    ws = np.array([0, rows[0]], np.int32)
+    total = int(rows.sum())
+    want = ogather(compact, total, bt_local, ws, ss, 4, bs)
+    bt = np.where(bt_local >= 0, bt_local + hi, -1).astype(np.int32)
+    dst = torch.zeros((total, 576), dtype=torch.bfloat16, device="cuda")
+    ggather(cache, dst, dev(bt), dev(ws), dev(ss))
+    torch.cuda.synchronize()
+    assert_same(host(dst), want, f"{fmt} gather from above 4 GiB")
+    del cache
+
+
+def test_perhead_cache_offsets_beyond_4gib(g, orc):
+    """The per-head pair on a cache of more than 5 GiB (H = 8, head size 128,
+    blocks of 16): tokens written into the last four blocks and gathered back
+    one request per token, against the oracle on those four blocks alone."""
+    H, hs, bs = 8, 128, 16
+    fd = hs // 2 + hs // 16
+    L = orc.kv_layout_split(bs, H, hs)
+    nb = (5 << 30) // L.block_stride + 1
+    hi = nb - 4
+    assert hi * L.block_stride > (1 << 32)
+    rng = np.random.default_rng(72)
+    T = 4 * bs
+    key = synth.bf16_bits(rng.standard_normal((T, H, hs), dtype=np.float32) * np.float32(3))
+    value = synth.bf16_bits(rng.standard_normal((T, H, hs), dtype=np.float32))
+    ks, vs = synth.global_scale(key), synth.global_scale(value)
+    local = rng.permutation(T).astype(np.int64)
+    local[::13] = -1
+    compact = np.full(4 * L.block_stride, 0xA5, np.uint8)
+    orc.reshape_and_cache_nvfp4(key, value, compact, local, 4, bs, L, ks, vs)
+    slots = np.where(local >= 0, local + hi * bs, -1)
+    print(f"per-head cache beyond 4 GiB: {nb} blocks, {nb * L.block_stride / 2**30:.2f} GiB", flush=True)
+    cache = torch.full((nb, 2, bs, H, fd), 0xA5, dtype=torch.uint8, device="cuda")
+    ks_d = torch.tensor([ks], dtype=torch.float32, device="cuda")
+    vs_d = torch.tensor([vs], dtype=torch.float32, device="cuda")
+    g.reshape_and_cache_nvfp4(dev(key), dev(value), cache, dev(slots), ks_d, vs_d)
+    torch.cuda.synchronize()
+    assert_same(host(cache[hi:]).reshape(-1), compact, "per-head entries above 4 GiB")
+    assert_same(host(cache[hi - 1]).reshape(-1), np.full(L.block_stride, 0xA5, np.uint8), "block below")
+
+    gl = synth.per_token_gather("kv-high", local, 4, bs)
+    ok, ov = orc.gather_upconvert_nvfp4_kv(compact, gl.total_tokens, gl.block_table, gl.workspace_starts,
+                                           gl.seq_starts, H, hs, 4, bs, L, ks, vs)
+    bt = (gl.block_table + hi).astype(np.int32)
+    ko = torch.zeros((gl.total_tokens, H, hs), dtype=torch.bfloat16, device="cuda")
+    vo = torch.zeros((gl.total_tokens, H, hs), dtype=torch.bfloat16, device="cuda")
+    g.gather_upconvert_nvfp4_kv(cache, ko, vo, dev(bt), dev(gl.workspace_starts), ks_d, vs_d,
+                                seq_starts=dev(gl.seq_starts))
+    torch.cuda.synchronize()
+    assert_same(host(ko), ok, "per-head K from above 4 GiB")
+    assert_same(host(vo), ov, "per-head V from above 4 GiB")
+    del cache
+
+
 def test_binding_rejects_unsafe_arguments(g):
     """Arguments the kernels could not bound are refused before any launch:
     a block table whose rows are not contiguous, a batch larger than the
