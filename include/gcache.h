@@ -289,7 +289,10 @@ typedef struct {
  * scales, V data, V scales, each contiguous): every side of a block is all
  * data rows [block_size][num_heads][head_size/2] followed by all scale rows
  * [block_size][num_heads][head_size/16]; block_stride = 2 * block_size *
- * num_heads * full_dim.  Returns GCACHE_ERR_SHAPE for bad sizes. */
+ * num_heads * full_dim.  Returns GCACHE_ERR_SHAPE for bad sizes.  The
+ * per-head kernels accept the layout when block_size * num_heads * full_dim
+ * (the side stride) is a multiple of 8; otherwise they return
+ * GCACHE_ERR_ALIGN. */
 int gcache_nvfp4_kv_split_layout(int32_t block_size, int32_t num_heads, int32_t head_size,
                                  gcache_nvfp4_kv_layout* out);
 
@@ -317,8 +320,9 @@ int gcache_nvfp4_kv_split_layout_hnd(int32_t block_size, int32_t num_heads, int3
  *
  *  key, value  bf16 [num_tokens, num_heads, head_size] with the given token
  *              and head strides (elements; multiples of 8, bases 16-byte aligned)
- *  kv_cache    uint8 cache; layout: host pointer (data and scale offsets and
- *              strides multiples of 8 and 1 bytes respectively)
+ *  kv_cache    uint8 cache, 16-byte aligned; layout: host pointer (data_offset,
+ *              the data strides, side_stride and block_stride multiples of 8
+ *              bytes, else GCACHE_ERR_ALIGN; scale offset and strides any)
  * Requirements: head_size a positive multiple of 16 (at most 1024),
  * num_heads > 0, block_size > 0.
  */

@@ -719,6 +719,110 @@ def test_perhead_cache_offsets_beyond_4gib(g, orc):
     del cache
 
 
+def _random_ds_case(rng):
+    """One seeded random DS-MLA case: geometry, strides, padding and gather
+    metadata drawn from ranges that cross the kernels' internal limits (tile
+    of 16, one wave of 64 requests, power-of-two and generic block sizes)."""
+    bs = int(rng.choice([1, 2, 3, 7, 16, 33, 64, 100, 128]))
+    nb = int(rng.integers(1, 41))
+    T = int(rng.integers(0, min(nb * bs, 700) + 1))
+    pad = int(rng.integers(0, T // 3 + 1))
+    ek, bk = int(rng.choice([0, 1, 3])), int(rng.choice([0, 2]))
+    xk = int(rng.choice([0, 2]))
+    B = int(rng.choice([1, 5, 63, 64, 65, 70]))
+    maxb = int(rng.integers(1, 9))
+    return dict(bs=bs, nb=nb, T=T, pad=pad, ek=ek, bk=bk, xk=xk, B=B, maxb=maxb,
+                dst_extra=int(rng.choice([0, 8])), seed=int(rng.integers(1 << 30)))
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "fp8"])
+def test_randomized_ds_sweep(g, orc, fmt):
+    """24 seeded random cases per format: block sizes 1..128 (power-of-two
+    and generic division), 0..700 tokens with random padding, padded entry
+    and block strides, strided inputs, 1..70 requests (both request searches)
+    with random lengths, empty requests, seq_starts and shared blocks, and a
+    wider dst row -- every cache byte and every output bit against the
+    oracle."""
+    eb = NV if fmt == "nvfp4" else F8
+    master = np.random.default_rng(4242 if fmt == "nvfp4" else 4343)
+    for n in range(24):
+        c = _random_ds_case(master)
+        print(f"random DS case {fmt} #{n}: {c}", flush=True)
+        rng = np.random.default_rng(c["seed"])
+        bs, nb, T = c["bs"], c["nb"], c["T"]
+        estr = eb + 16 * c["ek"]
+        bstr = bs * estr + 16 * c["bk"]
+        width = 584 + 8 * c["xk"]
+        buf = synth.bf16_bits(rng.standard_normal((T, width), dtype=np.float32)
+                              * np.exp(rng.standard_normal((T, 1), dtype=np.float32)))
+        kv_c, k_pe = buf[:, :512], buf[:, width - 64:]
+        slots = synth.padded_slots(rng, nb * bs, T, c["pad"])
+        if T:
+            bdev = dev(buf)
+            want, flat = run_ds_write(orc, fmt, kv_c, k_pe, slots, nb, bs, bstr, estr,
+                                      kv_dev=bdev[:, :512], pe_dev=bdev[:, width - 64:])
+        else:                           # nothing written: gather from an all-sentinel cache
+            want, flat = np.full(nb * bstr, 0xA5, np.uint8), filled_cache((nb * bstr,), 0xA5)
+        B, maxb = c["B"], c["maxb"]
+        L = rng.integers(0, maxb * bs + 1, size=B)
+        L[rng.random(B) < 0.15] = 0
+        s = np.array([rng.integers(0, l + 1) for l in L], np.int64)
+        rows = L - s
+        bt = np.full((B, maxb), -1, np.int32)
+        for b in range(B):
+            nblk = -(-int(L[b]) // bs)
+            bt[b, :nblk] = rng.integers(0, nb, size=nblk)      # blocks may repeat across requests
+        ws = np.concatenate([[0], np.cumsum(rows)[:-1]]).astype(np.int32)
+        gcase = synth.GatherCase(f"random-{n}", bt, ws, s.astype(np.int32), int(rows.sum()), nb, bs, L)
+        if gcase.total_tokens:
+            run_ds_gather(orc, fmt, want, flat, gcase, nb, bs, bstr, estr, dst_stride=576 + c["dst_extra"])
+
+
+def test_randomized_perhead_sweep(g, orc):
+    """16 seeded random per-head cases: 1..9 heads, head sizes 16..256 (all
+    multiples of 16), block sizes 1..32, the NHD or HND split layout or
+    [data | scale] rows per (token, head) (staged kernels whenever a token's
+    run is 16-byte aligned and at most 2048 bytes), 0..300 tokens with
+    padding, gathered back per token -- every byte and bit."""
+    master = np.random.default_rng(4444)
+    for n in range(16):
+        H = int(master.integers(1, 10))
+        hs = int(master.choice([16, 32, 48, 64, 80, 128, 256]))
+        bs = int(master.choice([1, 3, 8, 16, 32]))
+        nb = int(master.integers(1, 25))
+        T = int(master.integers(0, min(nb * bs, 300) + 1))
+        pad = int(master.integers(0, T // 4 + 1))
+        layout = str(master.choice(["nhd", "hnd", "rows"]))
+        if layout == "rows" and hs % 128:
+            hs = 128                    # [data | scale] rows keep 8-byte data alignment only at hs % 128 == 0
+        seed = int(master.integers(1 << 30))
+        print(f"random per-head case #{n}: H={H} hs={hs} bs={bs} nb={nb} T={T} pad={pad} layout={layout}",
+              flush=True)
+        rng = np.random.default_rng(seed)
+        if T == 0:
+            continue
+        key, value, slots = _kv_case(rng, T, H, hs, nb, bs, pad)
+        ks, vs = synth.global_scale(key), synth.global_scale(value)
+        if layout == "rows":
+            fd = hs // 2 + hs // 16
+            kw = dict(data_offset=0, data_token_stride=H * fd, data_head_stride=fd, scale_offset=hs // 2,
+                      scale_token_stride=H * fd, scale_head_stride=fd, side_stride=bs * H * fd,
+                      block_stride=2 * bs * H * fd)
+            L_orc, L_gpu = orc.KvLayout(**kw), g.NvFp4KvLayout(**kw)
+        else:
+            L_orc = orc.kv_layout_split(bs, H, hs, hnd=layout == "hnd")
+            L_gpu = g.nvfp4_kv_split_layout(bs, H, hs, hnd=layout == "hnd")
+        if any(v % 8 for v in (L_orc.data_offset, L_orc.data_token_stride, L_orc.data_head_stride,
+                               L_orc.side_stride, L_orc.block_stride)):
+            # e.g. a side of block_size * H * full_dim bytes that is not a multiple of 8: the
+            # kernels' 8-byte code accesses would be misaligned, so the library refuses
+            with pytest.raises(g.GcacheError) as e:
+                run_kv(orc, g, key, value, slots, nb, bs, L_orc, L_gpu, ks, vs)
+            assert e.value.status == -3
+            continue
+        run_kv(orc, g, key, value, slots, nb, bs, L_orc, L_gpu, ks, vs)
+
+
 def test_binding_rejects_unsafe_arguments(g):
     """Arguments the kernels could not bound are refused before any launch:
     a block table whose rows are not contiguous, a batch larger than the
