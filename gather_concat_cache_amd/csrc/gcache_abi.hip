@@ -278,7 +278,7 @@ int gcache_convert_req_index_to_global_index(const int32_t* req_id, int64_t num_
     p.ti_stride = token_indices_stride;
     p.out_stride = out_stride;
     p.topk = topk;
-    p.waves_per_row = (topk + 4 * kWave - 1) / (4 * kWave);
+    p.waves_per_row = 0;                                 // set by the launcher
     p.vec16 = topk % 4 == 0 && token_indices_stride % 4 == 0 && out_stride % 4 == 0 &&
               aligned(token_indices, 16) && aligned(out, 16);
     p.block_table = block_table;

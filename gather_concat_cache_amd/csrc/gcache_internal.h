@@ -82,7 +82,7 @@ struct SparseIndexParams {
     int32_t* out;                // [num_tokens, >=topk], row stride out_stride
     int64_t num_tokens, ti_stride, out_stride;
     int32_t topk;
-    int32_t waves_per_row;       // ceil(topk / 256)
+    int32_t waves_per_row;       // ceil(topk / indices per wave), set by the launcher
     int32_t vec16;               // 16-byte path allowed
     const int32_t* block_table;
     int64_t bt_stride;

@@ -9,16 +9,22 @@
 // is outside [0, num_blocks).
 //
 // Mapping: HBM-bound (4 bytes in, 4 bytes out per index; the block-table
-// reads hit in cache).  One wave per 256 indices of one token row: the row's
-// request id and block-table row are wave-uniform, each lane converts 4
-// consecutive indices with one 16-byte load and one 16-byte store when the
-// row is 16-byte aligned, element by element otherwise.
+// reads hit in cache).  Each wave takes a run of one token row, so the row's
+// request id and block-table row are wave-uniform.  When the rows are
+// 16-byte aligned (topk % 4 == 0) a wave converts 1024 indices: each lane
+// issues four 16-byte loads of 4 indices (consecutive lanes on consecutive
+// pieces, all in flight) and four 16-byte stores, which keeps enough bytes
+// in flight that the whole 4096 x 2048 conversion runs in about one round
+// of resident waves; otherwise a wave converts 256 indices element by
+// element.
 #include "gcache_internal.h"
 
 namespace gcache {
 
-constexpr int kIdxPerLane = 4;
-constexpr int kIdxPerWave = kIdxPerLane * kWave;
+constexpr int kIdxPerLane = 4;                          // element path
+constexpr int kIdxPerWave = kIdxPerLane * kWave;         // 256
+constexpr int kPiecesPerLane = 4;                        // 16-byte path: 4 x 4 indices per lane
+constexpr int kIdxPerWaveVec = 4 * kPiecesPerLane * kWave;   // 1024
 
 __device__ __forceinline__ int32_t global_slot(int32_t i, const int32_t* __restrict__ bt_row, bool req_ok,
                                                const SparseIndexParams& p) {
@@ -31,26 +37,38 @@ __device__ __forceinline__ int32_t global_slot(int32_t i, const int32_t* __restr
     return (int32_t)(blk * p.div.size + off);
 }
 
+template <bool VEC16>
 __global__ __launch_bounds__(kBlockThreads) void k_convert_req_index(SparseIndexParams p, int64_t wave0) {
     const int lane = lane_id();
     const int64_t w = wave0 + (int64_t)blockIdx.x * kWavesPerBlock + wave_id();
     const int64_t t = w / p.waves_per_row;
     if (t >= p.num_tokens) return;
-    const int k0 = (int)(w - t * p.waves_per_row) * kIdxPerWave + kIdxPerLane * lane;
+    const int run = (int)(w - t * p.waves_per_row);
     const int32_t req = p.req_id[t];                     // wave-uniform
     const bool req_ok = req >= 0 && req < p.batch;
     const int32_t* bt_row = p.block_table + (req_ok ? (int64_t)req * p.bt_stride : 0);
     const int32_t* src = p.token_indices + t * p.ti_stride;
     int32_t* dst = p.out + t * p.out_stride;
-    if (p.vec16) {                                       // topk % 4 == 0, rows 16-byte aligned
-        if (k0 >= p.topk) return;
-        const uint4 v = ld_stream16(src + k0);
-        const uint4 o = make_uint4((uint32_t)global_slot((int32_t)v.x, bt_row, req_ok, p),
-                                   (uint32_t)global_slot((int32_t)v.y, bt_row, req_ok, p),
-                                   (uint32_t)global_slot((int32_t)v.z, bt_row, req_ok, p),
-                                   (uint32_t)global_slot((int32_t)v.w, bt_row, req_ok, p));
-        st_stream16(dst + k0, o);
+    if (VEC16) {                                         // topk % 4 == 0, rows 16-byte aligned
+        const int kbase = run * kIdxPerWaveVec;
+        uint4 v[kPiecesPerLane];
+#pragma unroll
+        for (int j = 0; j < kPiecesPerLane; j++) {       // all loads first
+            const int k = kbase + 4 * (lane + kWave * j);
+            if (k < p.topk) v[j] = ld_stream16(src + k);
+        }
+#pragma unroll
+        for (int j = 0; j < kPiecesPerLane; j++) {
+            const int k = kbase + 4 * (lane + kWave * j);
+            if (k >= p.topk) continue;
+            const uint4 o = make_uint4((uint32_t)global_slot((int32_t)v[j].x, bt_row, req_ok, p),
+                                       (uint32_t)global_slot((int32_t)v[j].y, bt_row, req_ok, p),
+                                       (uint32_t)global_slot((int32_t)v[j].z, bt_row, req_ok, p),
+                                       (uint32_t)global_slot((int32_t)v[j].w, bt_row, req_ok, p));
+            st_stream16(dst + k, o);
+        }
     } else {
+        const int k0 = run * kIdxPerWave + kIdxPerLane * lane;
 #pragma unroll
         for (int j = 0; j < kIdxPerLane; j++)
             if (k0 + j < p.topk) dst[k0 + j] = global_slot(src[k0 + j], bt_row, req_ok, p);
@@ -58,7 +76,11 @@ __global__ __launch_bounds__(kBlockThreads) void k_convert_req_index(SparseIndex
 }
 
 hipError_t launch_convert_req_index(const SparseIndexParams& p, hipStream_t s) {
-    return launch_waves(k_convert_req_index, p.num_tokens * p.waves_per_row, s, p);
+    SparseIndexParams q = p;
+    const int per_wave = q.vec16 ? kIdxPerWaveVec : kIdxPerWave;
+    q.waves_per_row = (q.topk + per_wave - 1) / per_wave;
+    return q.vec16 ? launch_waves(k_convert_req_index<true>, q.num_tokens * q.waves_per_row, s, q)
+                   : launch_waves(k_convert_req_index<false>, q.num_tokens * q.waves_per_row, s, q);
 }
 
 }  // namespace gcache

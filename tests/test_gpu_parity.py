@@ -361,7 +361,10 @@ def test_sparse_index_conversion(g, orc):
                                                   gv["block_size"], case["num_blocks"])
         assert host(out).tolist() == case["out"]
     rng = np.random.default_rng(71)
-    for K, vec in ((37, False), (256, True), (300, False), (1024, True)):
+    # (topk, 16-byte path, extra out columns): partial and several waves per row on
+    # both paths, and a strided but aligned output on the 16-byte path
+    for K, vec, extra in ((37, False, 3), (256, True, 0), (300, False, 3), (1024, True, 0), (1500, True, 4),
+                          (4, True, 4), (2052, True, 0)):
         B, mb, bs, nb, T = 5, 9, 16, 60, 50
         bt = rng.integers(-2, nb + 3, size=(B, mb)).astype(np.int32)
         req = rng.integers(-1, B + 2, size=T).astype(np.int32)
@@ -370,12 +373,12 @@ def test_sparse_index_conversion(g, orc):
         wide = np.zeros((T, K + 5), np.int32)
         wide[:, :K] = ti
         ti_dev = dev(ti) if vec else dev(wide)[:, :K]
-        out = torch.full((T, K + 3), 7, dtype=torch.int32, device="cuda")
+        out = torch.full((T, K + extra), 7, dtype=torch.int32, device="cuda")
         got = g.convert_req_index_to_global_index(dev(req), ti_dev, dev(bt), bs, nb,
-                                                  out=out if not vec else None)
+                                                  out=out if extra else None)
         torch.cuda.synchronize()
         assert_same(host(got)[:, :K], want, f"sparse index K={K}")
-        if not vec:
+        if extra:
             assert np.all(host(out)[:, K:] == 7)          # bytes past topk untouched
     with pytest.raises(g.GcacheError):                    # req_id one longer than the rows
         g.convert_req_index_to_global_index(dev(np.zeros(6, np.int32)), dev(np.zeros((5, 8), np.int32)),
