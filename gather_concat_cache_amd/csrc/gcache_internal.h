@@ -120,18 +120,19 @@ inline hipError_t launch_waves(void (*kernel)(P, int64_t), int64_t waves, hipStr
     return hipSuccess;
 }
 
-// Launch `groups` one-shot workgroups of `kernel(params, group0)`: the
-// kernel's workgroup index is group0 + blockIdx.x (pieces of at most 2^24
-// workgroups, as above).
+// Launch `groups` one-shot workgroups of `threads` lanes of
+// `kernel(params, group0)`: the kernel's workgroup index is
+// group0 + blockIdx.x (pieces of at most 2^24 workgroups, as above).
 template <typename P>
-inline hipError_t launch_groups(void (*kernel)(P, int64_t), int64_t groups, hipStream_t s, const P& p) {
+inline hipError_t launch_groups(void (*kernel)(P, int64_t), int64_t groups, hipStream_t s, const P& p,
+                                int threads = kBlockThreads) {
     const int64_t kMaxBlocks = int64_t(1) << 24;
     for (int64_t b0 = 0; b0 < groups; b0 += kMaxBlocks) {
         const int64_t nb = groups - b0 < kMaxBlocks ? groups - b0 : kMaxBlocks;
         int64_t group0 = b0;
         void* args[] = {const_cast<P*>(&p), &group0};
         const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3((unsigned)nb),
-                                             dim3(kBlockThreads), args, 0, s);
+                                             dim3(threads), args, 0, s);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
