@@ -403,18 +403,19 @@ def measure_extras(torch, gc, g3, steps, dev_arr, cache3, perhead):
 
 def measure_ceilings(torch, ops, mix, reps=5):
     """For each DS-MLA op: the same-mix row copy of libgcache_bench.so (rows
-    of the op's read bytes in, its write bytes out, contiguous, 16-row LDS
-    tiles, no walk and no conversion) and the op itself, both cold (each
-    launch after a 2 GiB write that evicts L2 and the MALL), so the op can be
-    stated as a fraction of what a plain stream with its byte pattern reaches
-    on this device."""
+    of the op's read bytes in, its write bytes out, contiguous, staged
+    through LDS in groups of rows, no walk and no conversion) in several
+    workgroup shapes, and the op itself, all cold (each launch after a 2 GiB
+    write that evicts L2 and the MALL).  The fastest shape is the ceiling:
+    what a plain stream with the op's byte pattern reaches on this device."""
     import ctypes
     from gather_concat_cache_amd import build
     lib = ctypes.CDLL(build.BENCH_LIB)
     fn = lib.gcache_bench_copy_mix
     fn.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
-                   ctypes.c_void_p]
+                   ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
     fn.restype = ctypes.c_int
+    shapes = [(16, 256), (8, 256), (4, 128), (2, 64)]     # (rows per workgroup, threads)
     op_cold = measure_cold(torch, ops, reps)
     out = {}
     for name, nbytes, _, _ in ops:
@@ -422,17 +423,22 @@ def measure_ceilings(torch, ops, mix, reps=5):
         src = torch.empty(rows * rb, dtype=torch.uint8, device="cuda").fill_(0x3C)
         dst = torch.empty(rows * wb, dtype=torch.uint8, device="cuda")
         stream = torch.cuda.current_stream().cuda_stream
-
-        def copy():
-            rc = fn(src.data_ptr(), dst.data_ptr(), rows, rb, wb, stream)
-            if rc != 0:
-                raise RuntimeError(f"gcache_bench_copy_mix returned {rc}")
         cbytes = rows * (rb + wb)
-        ceil = measure_cold(torch, [(name, cbytes, rows, copy)], reps)[name]
+        per_shape = {}
+        for g, nt in shapes:
+            def copy(g=g, nt=nt):
+                rc = fn(src.data_ptr(), dst.data_ptr(), rows, rb, wb, g, nt, stream)
+                if rc != 0:
+                    raise RuntimeError(f"gcache_bench_copy_mix returned {rc}")
+            per_shape[f"{g}x{nt}"] = measure_cold(torch, [(name, cbytes, rows, copy)], reps)[name]
+        best = min(per_shape, key=lambda k: per_shape[k]["ms"])
+        ceil = per_shape[best]
         op_gbs = op_cold[name]["GB_per_s"]
         out[name] = {"rows": rows, "read_bytes": rb, "write_bytes": wb, "ceiling_ms": ceil["ms"],
-                     "ceiling_GB_per_s": ceil["GB_per_s"], "op_cold_ms": op_cold[name]["ms"],
-                     "op_cold_GB_per_s": op_gbs, "frac_of_ceiling": round(op_gbs / ceil["GB_per_s"], 4)}
+                     "ceiling_GB_per_s": ceil["GB_per_s"], "ceiling_shape": best,
+                     "shapes_GB_per_s": {k: v["GB_per_s"] for k, v in per_shape.items()},
+                     "op_cold_ms": op_cold[name]["ms"], "op_cold_GB_per_s": op_gbs,
+                     "frac_of_ceiling": round(op_gbs / ceil["GB_per_s"], 4)}
         del src, dst
     return out
 
@@ -475,16 +481,23 @@ def traffic_for(kernel):
         return None
 
 
-# kernel symbol (prefix up to the parameter list) -> op name used above
+# kernel symbol (prefix up to the parameter list, or up to the template
+# argument list of the write kernels) -> op name used above
 KERNEL_OPS = {
-    "gcache::k_write_nvfp4_ds_mla": "nvfp4_ds_mla_write",
-    "gcache::k_write_fp8_ds_mla": "fp8_ds_mla_write",
+    "void gcache::k_write_nvfp4_ds_mla": "nvfp4_ds_mla_write",
+    "void gcache::k_write_fp8_ds_mla": "fp8_ds_mla_write",
     "void gcache::k_gather_ds_mla<true>": "nvfp4_ds_mla_gather",
     "void gcache::k_reshape_and_cache_nvfp4<false>": "nvfp4_kv_write",
     "void gcache::k_gather_ds_mla<false>": "fp8_ds_mla_gather",
     "void gcache::k_gather_nvfp4_kv<false>": "nvfp4_kv_gather",
 }
 CALIBRATION_KERNEL = "CUDAFunctorOnSelf_add"
+
+
+def kernel_op(name):
+    """Op name of a demangled kernel symbol, or None."""
+    return next((op for k, op in KERNEL_OPS.items()
+                 if name.startswith(k + "(") or (not k.endswith(">") and name.startswith(k + "<"))), None)
 
 
 def write_traffic(fetch_dir, write_dir):
@@ -503,7 +516,7 @@ def write_traffic(fetch_dir, write_dir):
             if r["Counter_Name"] != counter:
                 continue
             name = r["Kernel_Name"]
-            key = next((op for k, op in KERNEL_OPS.items() if name.startswith(k + "(")), None)
+            key = kernel_op(name)
             if key is None and CALIBRATION_KERNEL in name:
                 key = "calibration"
             if key is not None:

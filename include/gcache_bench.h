@@ -22,17 +22,22 @@ extern "C" {
  * dst + r * write_bytes, built from the row's input 16-byte pieces (piece c
  * of the output is input piece c % (read_bytes / 16) when the output is
  * wider, the XOR of input pieces c, c + w, c + 2w, ... (w = write_bytes / 16)
- * when it is narrower), so every input byte is used.  Workgroups take 16
- * rows each and stage them through LDS like the DS-MLA gathers, but there is
- * no block-table walk and no format conversion.
+ * when it is narrower), so every input byte is used.  Workgroups of
+ * `threads` lanes take rows_per_group rows each and stage them through LDS
+ * like the cache kernels, with no block-table walk and no format
+ * conversion; bench.py times several workgroup shapes and keeps the
+ * fastest as the ceiling.
  *  src, dst  device pointers, 16-byte aligned, owned by the caller
  *  read_bytes, write_bytes  multiples of 16 in [16, 1152]
- * Returns 0, -1 for a null pointer, -2 for sizes out of range, -3 for a
- * misaligned pointer, -6 when the launch fails.  Enqueued on `stream`;
- * nothing is allocated or synchronized.
+ *  rows_per_group >= 1 with rows_per_group * read_bytes <= 18432,
+ *  threads a multiple of 64 in [64, 1024]
+ * Returns 0, -1 for a null pointer, -2 for sizes or shapes out of range,
+ * -3 for a misaligned pointer, -6 when the launch fails.  Enqueued on
+ * `stream`; nothing is allocated or synchronized.
  */
 int gcache_bench_copy_mix(const void* src, void* dst, int64_t rows, int32_t read_bytes,
-                          int32_t write_bytes, hipStream_t stream);
+                          int32_t write_bytes, int32_t rows_per_group, int32_t threads,
+                          hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -176,11 +176,14 @@ def test_bench_helper_library():
     assert sorted(set(re.findall(r"\b(gcache_[a-z0-9_]+)\s*\(", text))) == ["gcache_bench_copy_mix"]
     blib = C.CDLL(build.BENCH_LIB)
     f = blib.gcache_bench_copy_mix
-    f.argtypes = [C.c_void_p, C.c_void_p, C.c_int64, C.c_int32, C.c_int32, C.c_void_p]
+    f.argtypes = [C.c_void_p, C.c_void_p, C.c_int64, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_void_p]
     f.restype = C.c_int
-    assert f(None, None, 0, 352, 1152, None) == 0           # empty: no-op
-    assert f(None, A16, 10, 352, 1152, None) == -1
-    assert f(A16, A16, 10, 350, 1152, None) == -2
-    assert f(A16, A16, 10, 352, 1168, None) == -2
-    assert f(A16, A16, -1, 352, 1152, None) == -2
-    assert f(A16 + 8, A16, 10, 352, 1152, None) == -3
+    assert f(None, None, 0, 352, 1152, 16, 256, None) == 0           # empty: no-op
+    assert f(None, A16, 10, 352, 1152, 16, 256, None) == -1
+    assert f(A16, A16, 10, 350, 1152, 16, 256, None) == -2
+    assert f(A16, A16, 10, 352, 1168, 16, 256, None) == -2
+    assert f(A16, A16, -1, 352, 1152, 16, 256, None) == -2
+    assert f(A16, A16, 10, 352, 1152, 0, 256, None) == -2            # no rows per group
+    assert f(A16, A16, 10, 352, 1152, 16, 96, None) == -2            # not a whole number of waves
+    assert f(A16, A16, 10, 1152, 352, 17, 1024, None) == -2          # more than 18 KiB staged
+    assert f(A16 + 8, A16, 10, 352, 1152, 16, 256, None) == -3
