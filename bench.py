@@ -67,6 +67,13 @@ def parse():
                     help="with --stats-from: a bench.py output line of the same build, tabulated beside")
     ap.add_argument("--stats-extras", action="store_true",
                     help="with --stats-from: the run was --extras-only; write profiles/extras_kernels_stats.md")
+    ap.add_argument("--decode-write-only", action="store_true",
+                    help="profiling aid: run only the decode-batch writes (4096 tokens at random slots, both "
+                         "DS-MLA formats), --steps times each, then the --copy-calibration kernel; print their "
+                         "device times")
+    ap.add_argument("--decode-traffic-from", nargs=2, default=None, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="host only: turn two rocprofv3 --pmc runs of --decode-write-only (FETCH_SIZE, then "
+                         "WRITE_SIZE, each with --copy-calibration) into profiles/decode_write_hbm_traffic_pmc.md")
     return ap.parse_args()
 
 
@@ -111,6 +118,9 @@ def main():
     if args.stats_from:
         write_stats(args.stats_from, args.bench_json, args.stats_extras)
         return
+    if args.decode_traffic_from:
+        write_decode_traffic(*args.decode_traffic_from)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
               "(the path is token-parallel; see the design notes for how it shards).", file=sys.stderr)
@@ -125,6 +135,9 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
     torch.cuda.init()
+    if args.decode_write_only:
+        decode_write_only(torch, gc, args)
+        return
     dname = torch.cuda.get_device_name(0)
     t0 = time.time()
     w3, g3, w4, g4, w5, g5 = build_workloads()
@@ -233,16 +246,7 @@ def main():
         extras["same_mix_ceilings"] = measure_ceilings(torch, [o for o in ops if o[0] in mix], mix)
 
     if args.copy_calibration:
-        # a plain elementwise kernel that reads and writes exactly n bytes each
-        # (torch's copy_ of two device buffers goes to a DMA engine instead)
-        n = args.copy_calibration << 20
-        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
-        dst = torch.empty(n, dtype=torch.uint8, device="cuda")
-        torch.cuda.synchronize()
-        for _ in range(3):
-            torch.add(src, 1, out=dst)
-        torch.cuda.synchronize()
-        del src, dst
+        copy_calibration(torch, args.copy_calibration)
 
     cold = None
     if args.cold:
@@ -643,6 +647,104 @@ def write_stats(prof_dir, bench_json, extras=False):
     with open(os.path.join(ROOT, "profiles", name), "w") as f:
         f.write("\n".join(md) + "\n")
 
+
+def copy_calibration(torch, mib):
+    """A plain elementwise kernel that reads and writes exactly `mib` MiB
+    each, three times (torch's copy_ of two device buffers goes to a DMA
+    engine instead), so HBM counters can be scaled against known bytes."""
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    for _ in range(3):
+        torch.add(src, 1, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def decode_write_only(torch, gc, args):
+    """The decode-batch write workload alone (4096 tokens with lognormal
+    magnitudes into 4096 random slots of a 1024 x 64 cache, 82 padding), in
+    both DS-MLA formats: --steps launches each, then the calibration kernel.
+    Random single-token slots leave entries that start inside 128-byte lines,
+    so the counters show how much partial-line traffic the hardware adds."""
+    import synth
+    w2 = synth.config2()
+    kv = torch.from_numpy(np.ascontiguousarray(w2.kv_c).view(np.int16)).view(torch.bfloat16).cuda()
+    pe = torch.from_numpy(np.ascontiguousarray(w2.k_pe).view(np.int16)).view(torch.bfloat16).cuda()
+    sl = torch.from_numpy(np.ascontiguousarray(w2.slot_mapping)).cuda()
+    out = {}
+    for name, eb, fn in (("decode_batch_nvfp4_write", NV, gc.cache_write_nvfp4_ds_mla),
+                         ("decode_batch_fp8_write", F8, gc.cache_write_fp8_ds_mla)):
+        cache = torch.zeros((w2.num_blocks, w2.block_size, eb), dtype=torch.uint8, device="cuda")
+        ms = device_ms(torch, lambda: fn(kv, pe, cache, sl), max(1, args.steps))
+        out[name] = _extra(ms, ds_write_bytes(w2, eb), w2.num_tokens,
+                           f"{w2.num_tokens} decode tokens into {w2.num_blocks} x {w2.block_size} x {eb} B, "
+                           f"{int((w2.slot_mapping < 0).sum())} padding slots")
+        del cache
+    if args.copy_calibration:
+        copy_calibration(torch, args.copy_calibration)
+    print(json.dumps({"decode_writes": out}), flush=True)
+
+
+def write_decode_traffic(fetch_dir, write_dir):
+    """HBM bytes per launch of the decode-batch writes from two counter runs
+    of --decode-write-only (scaled by the calibration kernel, as for the
+    prefill pass) against their algorithmic bytes."""
+    import csv
+    import glob
+    import synth
+    from gather_concat_cache_amd.build import source_digest
+
+    names = {"nvfp4_ds_mla_write": "decode_batch_nvfp4_write", "fp8_ds_mla_write": "decode_batch_fp8_write"}
+
+    def per_kernel(d, counter):
+        (path,) = glob.glob(os.path.join(d, "*counter_collection.csv"))
+        vals = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            key = names.get(kernel_op(r["Kernel_Name"]))
+            if key is None and CALIBRATION_KERNEL in r["Kernel_Name"]:
+                key = "calibration"
+            if key is not None:
+                vals.setdefault(key, []).append(float(r["Counter_Value"]))
+        return vals
+
+    fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
+    cal_kib = 1024 * 1024.0
+    f_scale = cal_kib / float(np.mean(fetch["calibration"]))
+    w_scale = cal_kib / float(np.mean(write["calibration"]))
+    w2 = synth.config2()
+    valid = int((w2.slot_mapping >= 0).sum())
+    run = ("timeout -s KILL 120 rocprofv3 --pmc {c} --kernel-trace -f csv -d $R/{d} -o bench -- python3 "
+           "$R/bench.py --decode-write-only --steps 20 --copy-calibration 1024")
+    md = ["# HBM traffic per launch — decode-batch writes (4096 tokens at random slots)", "",
+          "Two counter runs, from /tmp on the MI355X box with the repository at $R, then the host-side summary:",
+          "", "```", run.format(c="FETCH_SIZE", d=os.path.relpath(fetch_dir, ROOT)),
+          run.format(c="WRITE_SIZE", d=os.path.relpath(write_dir, ROOT)),
+          f"python3 bench.py --decode-traffic-from {os.path.relpath(fetch_dir, ROOT)} "
+          f"{os.path.relpath(write_dir, ROOT)}", "```", "",
+          f"Kernel sources: library digest {source_digest()}. Workload: {w2.num_tokens} tokens ({valid} valid, "
+          f"{w2.num_tokens - valid} padding) into {w2.num_blocks} x {w2.block_size} entries at slots drawn "
+          "without replacement from all 65536, so most entries start inside a 128-byte line whose other "
+          "bytes belong to entries this launch does not write. Counters are scaled as for the prefill pass "
+          f"(fetch x{f_scale:.5f}, write x{w_scale:.5f}, from torch's elementwise add over 1 GiB in the same "
+          "run); each kernel: mean over its dispatches (one spin kernel and 20 launches each, plus the "
+          "first call).", "",
+          "| Kernel op | Dispatches | FETCH_SIZE (KiB, raw) | WRITE_SIZE (KiB, raw) | Read bytes (scaled) "
+          "| Algorithmic read | Written bytes (scaled) | Entry bytes | Write ratio |",
+          "|---|---|---|---|---|---|---|---|---|"]
+    for key, eb in (("decode_batch_nvfp4_write", NV), ("decode_batch_fp8_write", F8)):
+        fr, wr = float(np.mean(fetch[key])), float(np.mean(write[key]))
+        rb, wb = fr * 1024 * f_scale, wr * 1024 * w_scale
+        algo_r = valid * 1152 + w2.num_tokens * 8
+        algo_w = valid * eb
+        md.append(f"| {key} | {len(fetch[key])} / {len(write[key])} | {fr:,.1f} | {wr:,.1f} | {rb:,.0f} | "
+                  f"{algo_r:,} | {wb:,.0f} | {algo_w:,} | {wb / algo_w:.3f} |")
+    with open(os.path.join(ROOT, "profiles", "decode_write_hbm_traffic_pmc.md"), "w") as f:
+        f.write("\n".join(md) + "\n")
+    print("\n".join(md))
 
 # ---------------------------------------------------------------------------
 def _cpu_threads():
