@@ -424,7 +424,7 @@ def measure_extras(torch, gc, g3, steps, dev_arr, cache3, perhead):
     return out
 
 
-def measure_ceilings(torch, ops, mix, reps=5):
+def measure_ceilings(torch, ops, mix, reps=21):
     """For each DS-MLA op: the same-mix row copy of libgcache_bench.so (rows
     of the op's read bytes in, its write bytes out, contiguous, staged
     through LDS in groups of rows, no walk and no conversion) in several
@@ -466,7 +466,7 @@ def measure_ceilings(torch, ops, mix, reps=5):
     return out
 
 
-def measure_cold(torch, ops, reps=5):
+def measure_cold(torch, ops, reps=21):
     """Each kernel alone after writing a 2 GiB buffer (evicts L2 and the
     256 MB MALL); median over reps."""
     flush = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
