@@ -82,11 +82,11 @@ def parse():
 # ---------------------------------------------------------------------------
 def build_workloads():
     import synth
-    w3 = synth.config3_prefill()
-    g3 = synth.config3_gather()
-    w4 = synth.config4_prefill()
-    g4 = synth.config4_gather()
-    w5, g5 = synth.config5()
+    w3 = synth.nvfp4_prefill_write()
+    g3 = synth.nvfp4_prefill_gather()
+    w4 = synth.fp8_prefill_write()
+    g4 = synth.fp8_prefill_gather()
+    w5, g5 = synth.perhead_write_gather()
     return w3, g3, w4, g4, w5, g5
 
 
@@ -399,7 +399,7 @@ def measure_extras(torch, gc, g3, steps, dev_arr, cache3, perhead):
                                                 f"the per-head gather workload, {what}")
     del cache5
 
-    w2 = synth.config2()
+    w2 = synth.decode_batch_write()
     kv2, pe2 = (torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
                 for a in (w2.kv_c, w2.k_pe))
     sl2 = dev_arr(w2.slot_mapping)
@@ -575,7 +575,7 @@ def write_traffic(fetch_dir, write_dir):
     run = ("timeout -s KILL 120 rocprofv3 --pmc {c} --kernel-trace -f csv -d $R/{d} -o bench -- python3 "
            "$R/bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-extras --copy-calibration 1024")
     md = ["# HBM traffic per launch — all six kernels, prefill-context pass workload", "",
-          "Two counter runs (one counter each), from /tmp on the MI355X box with the repository at $R, "
+          "Two counter runs (one counter each), run from /tmp on an MI355X machine with the repository at $R, "
           "then the host-side summary:", "", "```",
           run.format(c="FETCH_SIZE", d=os.path.relpath(fetch_dir, ROOT)),
           run.format(c="WRITE_SIZE", d=os.path.relpath(write_dir, ROOT)),
@@ -618,7 +618,7 @@ def write_stats(prof_dir, bench_json, extras=False):
             "fp8_ds_mla write 1048576 tokens, nvfp4 gather 161766 rows, fp8 gather 219273 rows, per-head "
             "write 8192 tokens x 8 heads x 128, per-head gather 8110 rows.")
     md = [f"# rocprofv3 kernel statistics — {title}", "",
-          "Command (from /tmp on the MI355X box, repository at $R), then the host-side summary:", "",
+          "Command (run from /tmp on an MI355X machine, repository at $R), then the host-side summary:", "",
           "```", cmd, f"python3 bench.py --stats-from {os.path.relpath(prof_dir, ROOT)}"
           + (" --stats-extras" if extras else "")
           + (f" --bench-json {os.path.relpath(bench_json, ROOT)}" if bench_json else ""), "```", "",
@@ -669,7 +669,7 @@ def decode_write_only(torch, gc, args):
     Random single-token slots leave entries that start inside 128-byte lines,
     so the counters show how much partial-line traffic the hardware adds."""
     import synth
-    w2 = synth.config2()
+    w2 = synth.decode_batch_write()
     kv = torch.from_numpy(np.ascontiguousarray(w2.kv_c).view(np.int16)).view(torch.bfloat16).cuda()
     pe = torch.from_numpy(np.ascontiguousarray(w2.k_pe).view(np.int16)).view(torch.bfloat16).cuda()
     sl = torch.from_numpy(np.ascontiguousarray(w2.slot_mapping)).cuda()
@@ -715,12 +715,12 @@ def write_decode_traffic(fetch_dir, write_dir):
     cal_kib = 1024 * 1024.0
     f_scale = cal_kib / float(np.mean(fetch["calibration"]))
     w_scale = cal_kib / float(np.mean(write["calibration"]))
-    w2 = synth.config2()
+    w2 = synth.decode_batch_write()
     valid = int((w2.slot_mapping >= 0).sum())
     run = ("timeout -s KILL 120 rocprofv3 --pmc {c} --kernel-trace -f csv -d $R/{d} -o bench -- python3 "
            "$R/bench.py --decode-write-only --steps 20 --copy-calibration 1024")
     md = ["# HBM traffic per launch — decode-batch writes (4096 tokens at random slots)", "",
-          "Two counter runs, from /tmp on the MI355X box with the repository at $R, then the host-side summary:",
+          "Two counter runs, run from /tmp on an MI355X machine with the repository at $R, then the host-side summary:",
           "", "```", run.format(c="FETCH_SIZE", d=os.path.relpath(fetch_dir, ROOT)),
           run.format(c="WRITE_SIZE", d=os.path.relpath(write_dir, ROOT)),
           f"python3 bench.py --decode-traffic-from {os.path.relpath(fetch_dir, ROOT)} "

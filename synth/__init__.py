@@ -151,11 +151,13 @@ def per_token_gather(name, slot_mapping, num_blocks, block_size):
 
 
 # ---------------------------------------------------------------------------
-# The named workloads.  Seed of workload k is 1000 + k; a pre-fill write
-# draws NoPE from stream 0 and RoPE from stream 2 of that seed (row-chunked,
-# see normal_bf16_rows), the gather over it uses stream 1.
+# The named workloads, each with a fixed seed (tiny round trip 1001,
+# decode-batch write 1002, nvfp4 prefill pair 1003, fp8 prefill pair 1004,
+# per-head pair 1005).  A pre-fill write draws NoPE from stream 0 and RoPE
+# from stream 2 of its seed (row-chunked, see normal_bf16_rows); the gather
+# over it uses stream 1.
 # ---------------------------------------------------------------------------
-def config1():
+def tiny_round_trip():
     """Tiny round trip: 64 N(0,1) tokens, cache 8 x 64 x 352, 10% padding (6
     of 64), slots drawn from 512; gathered back per token and as one request
     over all 8 blocks."""
@@ -163,15 +165,15 @@ def config1():
     kv_c = _normal_bf16(rng, (64, NOPE))
     k_pe = _normal_bf16(rng, (64, ROPE))
     slots = padded_slots(rng, 512, 64, 6)
-    w = WriteCase("c1-write", kv_c, k_pe, slots, 8, 64)
-    g_tok = per_token_gather("c1-gather-per-token", slots, 8, 64)
-    g_all = GatherCase("c1-gather-all-blocks", np.arange(8, dtype=np.int32).reshape(1, 8),
+    w = WriteCase("tiny-write", kv_c, k_pe, slots, 8, 64)
+    g_tok = per_token_gather("tiny-gather-per-token", slots, 8, 64)
+    g_all = GatherCase("tiny-gather-all-blocks", np.arange(8, dtype=np.int32).reshape(1, 8),
                        np.zeros(1, np.int32), np.zeros(1, np.int32), 512, 8, 64,
                        np.array([512]))
     return w, g_tok, g_all
 
 
-def config2():
+def decode_batch_write():
     """Decode-batch write: 4096 tokens; NoPE = N(0,1) x per-token lognormal
     magnitude, 1% of elements x50; RoPE N(0,1); cache 1024 x 64; 4096 distinct
     slots of 65536, 82 (2%) padding."""
@@ -182,37 +184,37 @@ def config2():
     kv_c = bf16_bits(rng.standard_normal((T, NOPE), dtype=np.float32) * mag * out)
     k_pe = _normal_bf16(rng, (T, ROPE))
     slots = padded_slots(rng, 65536, T, 82)
-    return WriteCase("c2-decode-write", kv_c, k_pe, slots, 1024, 64)
+    return WriteCase("decode-batch-write", kv_c, k_pe, slots, 1024, 64)
 
 
-def config3_prefill():
+def nvfp4_prefill_write():
     """Pre-fill of the prefill-gather cache: 524288 N(0,1) tokens into every
     slot of 8192 blocks x 64 (slot_mapping = arange, no padding)."""
     T = 8192 * 64
-    return WriteCase("c3w-prefill-write", normal_bf16_rows(1003, 0, T, NOPE),
+    return WriteCase("nvfp4-prefill-write", normal_bf16_rows(1003, 0, T, NOPE),
                      normal_bf16_rows(1003, 2, T, ROPE), np.arange(T, dtype=np.int64), 8192, 64)
 
 
-def config3_gather():
+def nvfp4_prefill_gather():
     """Prefill gather: 16 requests, L ~ U[1024, 32768], seq_start ~ U[0, L/2],
     block tables over a shuffle of 8192 blocks (bs 64, 512 per request)."""
-    return prefill_gather(_rng(1003, 1), "c3-prefill-gather", 16, 1024, 32768, 8192, 64, 512)
+    return prefill_gather(_rng(1003, 1), "nvfp4-prefill-gather", 16, 1024, 32768, 8192, 64, 512)
 
 
-def config4_prefill():
+def fp8_prefill_write():
     """fp8_ds_mla pre-fill: 1048576 N(0,1) tokens into every slot of 16384 x 64."""
     T = 16384 * 64
-    return WriteCase("c4w-fp8-prefill-write", normal_bf16_rows(1004, 0, T, NOPE),
+    return WriteCase("fp8-prefill-write", normal_bf16_rows(1004, 0, T, NOPE),
                      normal_bf16_rows(1004, 2, T, ROPE), np.arange(T, dtype=np.int64), 16384, 64)
 
 
-def config4_gather():
+def fp8_prefill_gather():
     """fp8_ds_mla gather: 32 requests, L ~ U[512, 16384], seq_start ~ U[0, L/2],
     block tables over a shuffle of 16384 blocks (bs 64, 256 per request)."""
-    return prefill_gather(_rng(1004, 1), "c4-fp8-gather", 32, 512, 16384, 16384, 64, 256)
+    return prefill_gather(_rng(1004, 1), "fp8-prefill-gather", 32, 512, 16384, 16384, 64, 256)
 
 
-def config5():
+def perhead_write_gather():
     """Per-head NVFP4 K/V write: 8192 tokens, 8 KV heads of 128, K and V each
     N(0,1) x a per-head magnitude ~ U[0.1, 10] (drawn separately for K and V);
     cache 4096 blocks x 2 x 16 x 8 x 72; 8192 distinct slots of 65536, 82 (1%)
@@ -226,9 +228,9 @@ def config5():
     v_mag = rng.uniform(0.1, 10.0, size=H).astype(np.float32)
     value = bf16_bits(rng.standard_normal((T, H, hs), dtype=np.float32) * v_mag[None, :, None])
     slots = padded_slots(rng, 4096 * 16, T, 82)
-    w = KvWriteCase("c5-perhead-write", key, value, slots, 4096, 16,
+    w = KvWriteCase("perhead-write", key, value, slots, 4096, 16,
                     global_scale(key), global_scale(value))
-    g = per_token_gather("c5-perhead-gather", slots, 4096, 16)
+    g = per_token_gather("perhead-gather", slots, 4096, 16)
     return w, g
 
 

@@ -73,8 +73,8 @@ def test_host_entry_points_from_c(client_cpu, orc):
 
 def _cases():
     import synth
-    w1, _, g_all = synth.config1()
-    yield "config1-all-blocks", w1, g_all
+    w1, _, g_all = synth.tiny_round_trip()
+    yield "tiny_round_trip-all-blocks", w1, g_all
     rng = np.random.default_rng(61)
     nb, bs = 40, 64
     w = synth.random_write(62, 1500, nb, bs, 30)

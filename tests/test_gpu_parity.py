@@ -80,16 +80,16 @@ def run_ds_gather(orc, fmt, cache_np, cache_dev, gcase, nb, bs, bstr=None, estr=
 # nvfp4_ds_mla and fp8_ds_mla
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("fmt", ["nvfp4", "fp8"])
-def test_config1_round_trip(g, orc, fmt):
-    w, g_tok, g_all = synth.config1()
+def test_tiny_round_trip(g, orc, fmt):
+    w, g_tok, g_all = synth.tiny_round_trip()
     want, flat = run_ds_write(orc, fmt, w.kv_c, w.k_pe, w.slot_mapping, 8, 64)
     for gc_ in (g_tok, g_all):
         run_ds_gather(orc, fmt, want, flat, gc_, 8, 64)
 
 
 @pytest.mark.parametrize("fmt", ["nvfp4", "fp8"])
-def test_config2_decode_write(g, orc, fmt):
-    w = synth.config2()
+def test_decode_batch_write(g, orc, fmt):
+    w = synth.decode_batch_write()
     run_ds_write(orc, fmt, w.kv_c, w.k_pe, w.slot_mapping, w.num_blocks, w.block_size)
 
 
@@ -164,8 +164,8 @@ def test_full_size_prefill_write_and_gather(g, orc, fmt):
     """The benchmark's workloads: the 524288-token (nvfp4) / 1048576-token
     (fp8) pre-fill writes and the 16- / 32-request prefill gathers, whole
     cache and whole workspace compared."""
-    w = synth.config3_prefill() if fmt == "nvfp4" else synth.config4_prefill()
-    gcase = synth.config3_gather() if fmt == "nvfp4" else synth.config4_gather()
+    w = synth.nvfp4_prefill_write() if fmt == "nvfp4" else synth.fp8_prefill_write()
+    gcase = synth.nvfp4_prefill_gather() if fmt == "nvfp4" else synth.fp8_prefill_gather()
     want, flat = run_ds_write(orc, fmt, w.kv_c, w.k_pe, w.slot_mapping, w.num_blocks, w.block_size)
     del w
     run_ds_gather(orc, fmt, want, flat, gcase, gcase.num_blocks, gcase.block_size)
@@ -176,7 +176,7 @@ def test_request_counts_around_one_wave(g, orc, fmt):
     """Batches of 1, 63, 64 and 65 requests (the gather resolves requests
     with cross-lane reads up to 64 and searches memory beyond) and one
     single-row request per token of the decode batch (4014 requests)."""
-    w = synth.config2()
+    w = synth.decode_batch_write()
     want, flat = run_ds_write(orc, fmt, w.kv_c, w.k_pe, w.slot_mapping, w.num_blocks, w.block_size)
     run_ds_gather(orc, fmt, want, flat, synth.per_token_gather("per-token", w.slot_mapping, w.num_blocks,
                                                                w.block_size), w.num_blocks, w.block_size)
@@ -293,7 +293,7 @@ def test_bf16_comparator_gather(g, orc):
 def test_bf16_comparator_gather_full_size(g, orc):
     """The nvfp4 prefill gather's requests over a bf16 cache of the same
     geometry (8192 blocks x 64 x 1152 B): every row compared."""
-    gcase = synth.config3_gather()
+    gcase = synth.nvfp4_prefill_gather()
     cache = synth.normal_bf16_rows(1013, 0, gcase.num_blocks * gcase.block_size, 576)
     _bf16_gather_case(orc, g, cache.reshape(gcase.num_blocks, gcase.block_size, 576), gcase,
                       gcase.num_blocks, gcase.block_size, 576)
@@ -465,12 +465,12 @@ def run_kv(orc, g, key, value, slots, nb, bs, L_orc, L_gpu, ks, vs, key_dev=None
 
 
 @pytest.mark.parametrize("layout", ["split", "interleaved-rows"])
-def test_perhead_config5(g, orc, layout):
+def test_perhead_full_workload(g, orc, layout):
     """The per-head workload at full size (8192 tokens, 8 heads of 128,
     4096 blocks of 16), every byte and output bit: the default split layout
     (direct kernels) and [data | scale] rows per (token, head) (576-byte
     runs per token and side, the staged kernels), as the bench times them."""
-    w, _ = synth.config5()
+    w, _ = synth.perhead_write_gather()
     H, hs, bs = 8, 128, w.block_size
     if layout == "split":
         L_orc, L_gpu = orc.kv_layout_split(bs, H, hs), None
@@ -598,7 +598,7 @@ def test_side_stream_and_graph_replay(g, orc):
     gather pair captured in a HIP graph give the oracle's bytes; the graph is
     replayed several times with eager work in between and every replay is
     checked (the kernels allocate nothing and issue no memset)."""
-    w, g_tok, _ = synth.config1()
+    w, g_tok, _ = synth.tiny_round_trip()
     want = np.full(8 * 64 * NV, 0xA5, np.uint8)
     orc.write_nvfp4_ds_mla(w.kv_c, w.k_pe, want, w.slot_mapping, 8, 64)
     rows = orc.gather_nvfp4_ds_mla(want, g_tok.total_tokens, g_tok.block_table, g_tok.workspace_starts,

@@ -20,9 +20,9 @@ SRC = os.path.join(ROOT, "oracle", "gcache_oracle.c")
 MUTANTS = [
     ("nibble order", "entry[k] = (uint8_t)(q[2 * k] | (q[2 * k + 1] << 4));",
      "entry[k] = (uint8_t)(q[2 * k + 1] | (q[2 * k] << 4));",
-     [ops.test_nvfp4_block_hand_vectors, ops.test_nvfp4_write_and_gathers_vs_brute_force_config1]),
+     [ops.test_nvfp4_block_hand_vectors, ops.test_nvfp4_write_and_gathers_vs_brute_force_tiny]),
     ("scale divisor", "uint8_t sf = orc_e4m3_encode(amax / 6.0f);", "uint8_t sf = orc_e4m3_encode(amax / 4.0f);",
-     [ops.test_nvfp4_block_hand_vectors, ops.test_page_tolerances_config1_and_config2]),
+     [ops.test_nvfp4_block_hand_vectors, ops.test_page_tolerances_tiny_and_decode_workloads]),
     ("walk drops the request start", "+ (r - ws[req]);", "+ r;",
      [ops.test_gather_walk_hand_vectors, ops.test_address_tags_pin_the_walk]),
     ("fp8 group index", "* sc[i / F8_GROUP];", "* sc[0];",

@@ -157,9 +157,9 @@ def _tight_bounds(x, s, deq):
     return int((~ok).sum())
 
 
-def test_page_tolerances_config1_and_config2(orc):
-    w1, _, _ = synth.config1()
-    w2 = synth.config2()
+def test_page_tolerances_tiny_and_decode_workloads(orc):
+    w1, _, _ = synth.tiny_round_trip()
+    w2 = synth.decode_batch_write()
     for w in (w1, w2):
         valid = w.slot_mapping >= 0
         cache = np.full(w.num_blocks * w.block_size * NV, 0xA5, np.uint8)
@@ -171,8 +171,8 @@ def test_page_tolerances_config1_and_config2(orc):
             assert excluded > 0          # the x50 outliers of lognormal tokens saturate some scales
 
 
-def test_nvfp4_write_and_gathers_vs_brute_force_config1(orc):
-    w, g_tok, g_all = synth.config1()
+def test_nvfp4_write_and_gathers_vs_brute_force_tiny(orc):
+    w, g_tok, g_all = synth.tiny_round_trip()
     cache = np.full(w.num_blocks * w.block_size * NV, 0xA5, np.uint8)
     orc.write_nvfp4_ds_mla(w.kv_c, w.k_pe, cache, w.slot_mapping, w.num_blocks, w.block_size)
     want = np.full_like(cache, 0xA5)
@@ -280,7 +280,7 @@ def test_perhead_write_and_gather_vs_brute_force(orc, layout):
 def test_perhead_with_unit_scale_matches_ds_mla_nope(orc):
     """Special case: a 512-wide head with gs = 1 quantizes exactly like the
     DS-MLA NoPE part (same block rule, same nibble order, same scales)."""
-    w, _, _ = synth.config1()
+    w, _, _ = synth.tiny_round_trip()
     T = 16
     kv_c, k_pe = w.kv_c[:T], w.k_pe[:T]
     ent = _write_one(orc, np.ascontiguousarray(kv_c), np.ascontiguousarray(k_pe))
@@ -333,7 +333,7 @@ def test_bf16_comparator_gather_vs_brute_force(orc):
 
 
 def test_padding_and_untouched_bytes_keep_sentinels(orc):
-    w = synth.config2()
+    w = synth.decode_batch_write()
     for fill in (0xA5, 0x5A):
         for fmt, eb in (("nvfp4", NV), ("fp8", F8)):
             cache = np.full(w.num_blocks * w.block_size * eb, fill, np.uint8)
@@ -345,7 +345,7 @@ def test_padding_and_untouched_bytes_keep_sentinels(orc):
 
 
 def test_invalid_inputs_are_rejected(orc):
-    w, _, _ = synth.config1()
+    w, _, _ = synth.tiny_round_trip()
     cache = np.zeros(8 * 64 * NV, np.uint8)
     dup = w.slot_mapping.copy()
     dup[1] = dup[0] = 5
