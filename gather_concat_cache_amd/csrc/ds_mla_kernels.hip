@@ -9,8 +9,8 @@
 // All four kernels are HBM-bound streams with no contraction.  What bounds
 // them on MI355X is latency (bytes in flight), the cache state left by the
 // previous op and the shape of the write front, so:
-//   - every workgroup is one-shot (one group of 16 tokens or rows, no
-//     grid-stride loop): the groups in flight then cover a compact,
+//   - every workgroup is one-shot (one small group of tokens or 16 rows,
+//     no grid-stride loop): the groups in flight then cover a compact,
 //     advancing window of addresses, which the memory system writes far
 //     faster than the scattered fronts of persistent loops;
 //   - every wave issues all of its loads before it needs them;
