@@ -740,7 +740,7 @@ def _random_ds_case(rng):
 
 @pytest.mark.parametrize("fmt", ["nvfp4", "fp8"])
 def test_randomized_ds_sweep(g, orc, fmt):
-    """24 seeded random cases per format: block sizes 1..128 (power-of-two
+    """96 seeded random cases per format: block sizes 1..128 (power-of-two
     and generic division), 0..700 tokens with random padding, padded entry
     and block strides, strided inputs, 1..70 requests (both request searches)
     with random lengths, empty requests, seq_starts and shared blocks, and a
@@ -748,7 +748,7 @@ def test_randomized_ds_sweep(g, orc, fmt):
     oracle."""
     eb = NV if fmt == "nvfp4" else F8
     master = np.random.default_rng(4242 if fmt == "nvfp4" else 4343)
-    for n in range(24):
+    for n in range(96):
         c = _random_ds_case(master)
         print(f"random DS case {fmt} #{n}: {c}", flush=True)
         rng = np.random.default_rng(c["seed"])
@@ -782,13 +782,13 @@ def test_randomized_ds_sweep(g, orc, fmt):
 
 
 def test_randomized_perhead_sweep(g, orc):
-    """16 seeded random per-head cases: 1..9 heads, head sizes 16..256 (all
+    """48 seeded random per-head cases: 1..9 heads, head sizes 16..256 (all
     multiples of 16), block sizes 1..32, the NHD or HND split layout or
     [data | scale] rows per (token, head) (staged kernels whenever a token's
     run is 16-byte aligned and at most 2048 bytes), 0..300 tokens with
     padding, gathered back per token -- every byte and bit."""
     master = np.random.default_rng(4444)
-    for n in range(16):
+    for n in range(48):
         H = int(master.integers(1, 10))
         hs = int(master.choice([16, 32, 48, 64, 80, 128, 256]))
         bs = int(master.choice([1, 3, 8, 16, 32]))
