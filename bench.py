@@ -244,6 +244,13 @@ def main():
         mix = {"nvfp4_ds_mla_write": (w3.num_tokens, 1152, NV), "fp8_ds_mla_write": (w4.num_tokens, 1152, F8),
                "nvfp4_ds_mla_gather": (g3.total_tokens, NV, 1152), "fp8_ds_mla_gather": (g4.total_tokens, F8, 1152)}
         extras["same_mix_ceilings"] = measure_ceilings(torch, [o for o in ops if o[0] in mix], mix)
+        extras["gather_streaming_rate"] = measure_gather_streaming(torch, gc, [
+            ("nvfp4_ds_mla_gather", g3.total_tokens, NV,
+             lambda n: gc.cache_gather_upconvert_nvfp4_ds_mla(d["cache3"], d["dst3"][:n], d["bt3"], d["ws3"],
+                                                             d["ss3"])),
+            ("fp8_ds_mla_gather", g4.total_tokens, F8,
+             lambda n: gc.cache_gather_upconvert_fp8_ds_mla(d["cache4"], d["dst4"][:n], d["bt4"], d["ws4"],
+                                                           d["ss4"]))])
 
     if args.copy_calibration:
         copy_calibration(torch, args.copy_calibration)
@@ -463,6 +470,27 @@ def measure_ceilings(torch, ops, mix, reps=21):
                      "op_cold_ms": op_cold[name]["ms"], "op_cold_GB_per_s": op_gbs,
                      "frac_of_ceiling": round(op_gbs / ceil["GB_per_s"], 4)}
         del src, dst
+    return out
+
+
+def measure_gather_streaming(torch, gc, cases, reps=21):
+    """Each DS-MLA gather over all of its workspace rows and over the first
+    half of them (the same requests, cut at half the rows), both cold.  The
+    difference gives the rate at which the kernel streams once running
+    (bytes of the second half / extra time) and the fixed cost of a launch
+    (the full time less the full bytes at that rate; it includes the few
+    microseconds a HIP event pair adds)."""
+    out = {}
+    for name, rows, entry, run in cases:
+        half = rows // 2
+        per_row = entry + 1152
+        t = measure_cold(torch, [("full", rows * per_row, rows, lambda: run(rows)),
+                                 ("half", half * per_row, half, lambda: run(half))], reps)
+        extra_ms = t["full"]["ms"] - t["half"]["ms"]
+        rate = (rows - half) * per_row / (extra_ms * 1e6) if extra_ms > 0 else float("nan")
+        out[name] = {"rows": rows, "ms_full": t["full"]["ms"], "ms_half": t["half"]["ms"],
+                     "streaming_GB_per_s": round(rate, 1), "streaming_frac_of_hbm_peak": round(rate / HBM_PEAK_GBS, 4),
+                     "fixed_ms": round(t["full"]["ms"] - rows * per_row / (rate * 1e6), 5)}
     return out
 
 
