@@ -66,3 +66,16 @@ def test_kernel_names_map_to_ops():
         "fp8_ds_mla_gather"
     assert bench.kernel_op("void gcache::k_gather_nvfp4_kv<true>(gcache::KvGatherParams, long)") is None
     assert bench.kernel_op("gcache::k_gather_bf16(gcache::DsMlaGatherParams, long)") is None
+
+
+def test_more_than_one_gpu_is_refused():
+    """bench.py measures one GPU: --gpus above 1 exits with status 2 and a
+    message, before touching any device."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and not r.stdout.strip()
