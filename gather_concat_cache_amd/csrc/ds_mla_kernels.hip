@@ -16,8 +16,9 @@
 //   - every wave issues all of its loads before it needs them;
 //   - every store is a full 16-byte piece: the odd-sized parts of an entry
 //     (each lane's NoPE code bytes, scale bytes or fp32 scales, RoPE codes)
-//     are assembled in LDS first, so the cache sees whole 1 KiB runs
-//     instead of partial lines written by several instructions;
+//     are assembled in LDS first, so the cache sees whole contiguous runs
+//     (up to 1 KiB per store instruction) instead of partial lines written
+//     by several instructions;
 //   - inputs and outputs use streaming (nontemporal) accesses.
 // Mappings:
 //   nvfp4 write : one wave per workgroup and two tokens per wave; 8 values
