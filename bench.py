@@ -235,6 +235,7 @@ def main():
     for name, nbytes, units, _ in ops:
         ms = kern_ms[name]
         kernels[name] = {"ms": round(ms, 5), "bytes": nbytes, "units": units,
+                         "units_per_s": round(units / (ms * 1e-3), 1),
                          "GB_per_s": round(nbytes / (ms * 1e6), 1),
                          "frac_of_hbm_peak": round(nbytes / (ms * 1e6) / HBM_PEAK_GBS, 4)}
 
