@@ -260,6 +260,14 @@ def main():
     if args.cold:
         cold = measure_cold(torch, ops)
 
+    # every op against the same HBM roofline (per-kernel pass durations), with
+    # the measured HBM bytes per launch where the counters match this build
+    roofline_by_op = {name: {"bound": "hbm", "achieved": round(nbytes / (kern_ms[name] * 1e6), 1),
+                             "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": round(nbytes / (kern_ms[name] * 1e6) / HBM_PEAK_GBS, 4),
+                             "algorithmic_bytes": nbytes, "traffic": traffic_for(name)}
+                      for name, nbytes, _, _ in ops}
+
     dom = ops[dom_i]
     achieved = dom[1] / (dom_ms * 1e6)
     roofline = {"kernel": dom[0], "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
@@ -282,6 +290,7 @@ def main():
                    "step_bytes": step_bytes, "ops": [o[0] for o in ops], "device": dname},
         "kernels": kernels,
         "roofline": roofline,
+        "roofline_by_op": roofline_by_op,
         "cpu_baseline": cpu,
         "extras": extras,
         "input_generation_s": round(gen_s, 2),
