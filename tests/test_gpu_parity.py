@@ -87,6 +87,65 @@ def test_tiny_round_trip(g, orc, fmt):
         run_ds_gather(orc, fmt, want, flat, gc_, 8, 64)
 
 
+def test_rounding_order_hand_vectors(g, orc):
+    """The hand-derived rounding-order cases through the kernels: the fp8
+    write multiplies by the reciprocal scale, the fp8 gather rounds the
+    binary32 product to bf16, the per-head scale is (amax / 6) / gs and the
+    per-head dequant rounds twice.  Each result is compared with the
+    fixture's value and with the oracle."""
+    from conftest import load_golden
+    from test_oracle_ops import fp8_gather_rounding_entry, golden_gs
+    f8 = load_golden("fp8_ds_mla_vectors.json")
+    w = f8["write_rounding"]
+    row = np.zeros((1, 512), np.float32)
+    row[0, :len(w["values_head"])] = w["values_head"]
+    kv_c = synth.bf16_bits(row)
+    k_pe = np.zeros((1, 64), np.uint16)
+    want, flat = run_ds_write(orc, "fp8", kv_c, k_pe, np.zeros(1, np.int64), 1, 1, fill=0)
+    e = host(flat)
+    assert [f"{c:#04x}" for c in e[:len(w["codes_head"])]] == w["codes_head"]
+    assert e[512:516].tobytes().hex() == w["scale_le"]
+    one = synth.GatherCase("one row", np.zeros((1, 1), np.int32), np.zeros(1, np.int32),
+                           np.zeros(1, np.int32), 1, 1, 1, np.ones(1, np.int64))
+    run_ds_gather(orc, "fp8", want, flat, one, 1, 1)
+    r = f8["gather_rounding"]
+    entry = fp8_gather_rounding_entry(r)
+    flat = dev(entry)
+    run_ds_gather(orc, "fp8", entry, flat, one, 1, 1)
+    _, _, ggather = _ds_pair("fp8")
+    dst = dev(np.zeros((1, 576), np.uint16))
+    ggather(_cache_view(flat, 1, 1, F8, F8), dst, dev(one.block_table), dev(one.workspace_starts), None)
+    torch.cuda.synchronize()
+    assert [f"{b:#06x}" for b in host(dst)[0, :len(r["codes"])]] == r["dequant_bf16"]
+
+    # per-head: one token, one head of 16 values; data at 0, scale byte at 8
+    kw = dict(data_offset=0, data_token_stride=8, data_head_stride=8, scale_offset=8, scale_token_stride=1,
+              scale_head_stride=1, side_stride=16, block_stride=32)
+    L_orc, L_gpu = orc.KvLayout(**kw), g.NvFp4KvLayout(**kw)
+    for h in load_golden("perhead_vectors.json")["heads"]:
+        gs = golden_gs(h)
+        key = synth.bf16_bits(np.array(h["values"], np.float32).reshape(1, 1, 16))
+        run_kv(orc, g, key, key, np.zeros(1, np.int64), 1, 1, L_orc, L_gpu, gs, gs)
+        flat = filled_cache((32,), 0xA5)
+        cache5 = torch.as_strided(flat, (1, 2, 1, 1, 9), (32, 16, 9, 9, 1))
+        gs_d = torch.tensor([gs], dtype=torch.float32, device="cuda")
+        g.reshape_and_cache_nvfp4(dev(key), dev(key), cache5, dev(np.zeros(1, np.int64)), gs_d, gs_d,
+                                  layout=L_gpu)
+        ko = torch.zeros((1, 1, 16), dtype=torch.bfloat16, device="cuda")
+        vo = torch.zeros_like(ko)
+        g.gather_upconvert_nvfp4_kv(cache5, ko, vo, dev(np.zeros((1, 1), np.int32)), dev(np.zeros(1, np.int32)),
+                                    gs_d, gs_d, layout=L_gpu)
+        torch.cuda.synchronize()
+        c = host(flat)
+        for side in (0, 1):
+            assert c[16 * side:16 * side + 8].tobytes().hex() == h["data"], h["name"]
+            assert c[16 * side + 8] == int(h["scale_byte"], 16), h["name"]
+        k = host(ko)[0, 0]
+        assert np.array_equal(host(vo)[0, 0], k), h["name"]
+        if "dequant_bits" in h:
+            assert [f"{b:#06x}" for b in k] == h["dequant_bits"], h["name"]
+
+
 @pytest.mark.parametrize("fmt", ["nvfp4", "fp8"])
 def test_decode_batch_write(g, orc, fmt):
     w = synth.decode_batch_write()

@@ -16,6 +16,13 @@ from conftest import ROOT
 
 SRC = os.path.join(ROOT, "oracle", "gcache_oracle.c")
 
+# A binary32 value rounded to odd from an exact double: rounding it to bf16
+# afterwards equals one correct rounding of the exact value (binary32 keeps
+# more than two extra bits), so a mutant built with it rounds only once.
+ROUND_ONCE = ("({ double d_ = (%s); float f_ = (float)d_; "
+              "if (fabs((double)f_) > fabs(d_)) f_ = nextafterf(f_, 0.0f); "
+              "if ((double)f_ != d_) { uint32_t u_; memcpy(&u_, &f_, 4); u_ |= 1u; memcpy(&f_, &u_, 4); } f_; })")
+
 # (name, text in the oracle source, replacement, pins that must catch it)
 MUTANTS = [
     ("nibble order", "entry[k] = (uint8_t)(q[2 * k] | (q[2 * k + 1] << 4));",
@@ -38,6 +45,20 @@ MUTANTS = [
      [sparse.test_hand_vectors, sparse.test_random_vs_brute_force]),
     ("HND token stride", "out->data_token_stride = data_row;", "out->data_token_stride = data_per_head;",
      [views.test_split_layout_hand_values]),
+    # rounding-order readings: only the hand vectors are listed, the brute
+    # force restates the same formulas
+    ("fp8 write divides by the scale", "entry[i] = orc_e4m3_encode(orc_bf16_to_f32(nope[i]) * inv);",
+     "entry[i] = orc_e4m3_encode(orc_bf16_to_f32(nope[i]) / sc);",
+     [ops.test_fp8_rounding_order_hand_vectors]),
+    ("fp8 dequant rounds once", "float v = orc_e4m3_decode(entry[i]) * sc[i / F8_GROUP];",
+     "float v = " + ROUND_ONCE % "(double)orc_e4m3_decode(entry[i]) * (double)sc[i / F8_GROUP]" + ";",
+     [ops.test_fp8_rounding_order_hand_vectors]),
+    ("per-head scale as amax / (6 gs)", "uint8_t sf = orc_e4m3_encode((amax / 6.0f) / gs);",
+     "uint8_t sf = orc_e4m3_encode(amax / (6.0f * gs));",
+     [ops.test_perhead_hand_vectors]),
+    ("per-head dequant rounds once", "o[i] = orc_f32_to_bf16_rne(code_times_scale * gs);",
+     "o[i] = orc_f32_to_bf16_rne(" + ROUND_ONCE % "(double)code_times_scale * (double)gs" + ");",
+     [ops.test_perhead_hand_vectors]),
 ]
 
 

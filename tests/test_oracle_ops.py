@@ -94,23 +94,68 @@ def test_fp8_hand_vectors(orc):
     assert list(d[0, 512:514]) == [0x3F80, 0xC020]
 
 
+def golden_gs(h):
+    """A fixture's per-tensor scale: exact binary32 bits when given, else a
+    value that is exact in binary32."""
+    if "gs_bits" in h:
+        return float(np.array(int(h["gs_bits"], 16), np.uint32).view(np.float32))
+    return float(np.float32(h["gs"]))
+
+
 def test_perhead_hand_vectors(orc):
+    """Per-head blocks through the oracle's write and gather.  The last two
+    heads take a per-tensor scale that is not a power of two: one fixes the
+    order of the scale computation ((amax / 6) / gs), the other the two
+    roundings of the dequant (binary32, then bf16)."""
     g = load_golden("perhead_vectors.json")
     for h in g["heads"]:
+        gs = golden_gs(h)
         key = bf16_bits(np.array(h["values"], np.float32).reshape(1, 1, 16))
         L = orc.kv_layout_split(1, 1, 16)
         cache = np.full(2 * 9, 0xA5, np.uint8)
-        orc.reshape_and_cache_nvfp4(key, key, cache, np.zeros(1, np.int64), 1, 1, L, h["gs"], h["gs"])
+        orc.reshape_and_cache_nvfp4(key, key, cache, np.zeros(1, np.int64), 1, 1, L, gs, gs)
         for side in (0, 1):
             assert cache[9 * side:9 * side + 8].tobytes().hex() == h["data"], h["name"]
             assert cache[9 * side + 8] == int(h["scale_byte"], 16), h["name"]
         k, v = orc.gather_upconvert_nvfp4_kv(cache, 1, np.zeros((1, 1), np.int32), np.zeros(1, np.int32),
-                                             None, 1, 16, 1, 1, L, h["gs"], h["gs"])
+                                             None, 1, 16, 1, 1, L, gs, gs)
+        assert np.array_equal(v, k), h["name"]
         if "dequant_bf16" in h:
-            assert np.all(k == int(h["dequant_bf16"], 16)) and np.all(v == k)
+            assert np.all(k == int(h["dequant_bf16"], 16)), h["name"]
+        elif "dequant_bits" in h:
+            want = np.array([int(b, 16) for b in h["dequant_bits"]], np.uint16)
+            assert np.array_equal(k[0, 0], want), h["name"]
         else:
             want = np.array(h["dequant"], np.float32)
-            assert np.array_equal(bf16_to_f32(k[0, 0]).view(np.uint32), want.view(np.uint32))
+            assert np.array_equal(bf16_to_f32(k[0, 0]).view(np.uint32), want.view(np.uint32)), h["name"]
+
+
+def fp8_gather_rounding_entry(case):
+    """The hand-built fp8_ds_mla entry of the gather rounding case: its codes
+    lead group 0, whose scale has the given bits; everything else is zero."""
+    e = np.zeros(F8, np.uint8)
+    e[:len(case["codes"])] = [int(c, 16) for c in case["codes"]]
+    e[512:516] = np.array([int(case["scale_bits"], 16)], "<u4").view(np.uint8)
+    return e
+
+
+def test_fp8_rounding_order_hand_vectors(orc):
+    """fp8_ds_mla with a scale that is not a power of two: the write
+    multiplies by the binary32 reciprocal of the scale (not a division), and
+    the gather rounds the binary32 product to bf16 (two roundings)."""
+    g = load_golden("fp8_ds_mla_vectors.json")
+    w = g["write_rounding"]
+    row = np.zeros((1, 512), np.float32)
+    row[0, :len(w["values_head"])] = w["values_head"]
+    e = _write_one(orc, bf16_bits(row), fmt="fp8")[0]
+    assert [f"{c:#04x}" for c in e[:len(w["codes_head"])]] == w["codes_head"]
+    assert e[512:516].tobytes().hex() == w["scale_le"]
+    d = orc.gather_fp8_ds_mla(e.copy(), 1, np.zeros((1, 1), np.int32), np.zeros(1, np.int32), None, 1, 1)
+    assert list(bf16_to_f32(d[0, :len(w["dequant_head"])])) == w["dequant_head"]
+    r = g["gather_rounding"]
+    d = orc.gather_fp8_ds_mla(fp8_gather_rounding_entry(r), 1, np.zeros((1, 1), np.int32),
+                              np.zeros(1, np.int32), None, 1, 1)
+    assert [f"{b:#06x}" for b in d[0, :len(r["codes"])]] == r["dequant_bf16"]
 
 
 def test_gather_walk_hand_vectors(orc):
