@@ -15,11 +15,14 @@ synthetic workload, inputs resident in HBM:
 (writes and the gathers over their caches are interleaved so that a gather
 does not find its freshly written cache in the 256 MB last-level cache).
 
-Prints ONE JSON line: the whole step's effective HBM throughput (algorithmic
-bytes / wall time per step over the timed K steps, which record HIP events
-around the dominant kernel only), per-kernel HIP-event durations and GB/s
-(from a separate pass of K steps with events around every kernel), the
-roofline of the dominant kernel (its events in the timed region) and the CPU
+Prints ONE JSON line.  `value` is the metric: the algorithmic bytes of the
+NVFP4 DS-MLA write (op 1) and gather-upconvert (op 3) over their kernel time,
+both kernels timed live inside the timed region by HIP events bound to their
+own begin and end (gcache_time_next_launch: no enqueue gap, so the figures
+agree with rocprofv3's kernel durations); `roofline` is the gather's,
+`roofline_write` the write's.  Also: the whole step's throughput (all six
+ops' bytes / wall time per step), per-kernel durations of every op from a
+separate pass of K steps, every op against the HBM roofline, and the CPU
 oracle's throughput on a bounded sample of the same workloads.
 """
 import argparse
@@ -35,6 +38,53 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak, GB/s
 NV, F8 = 352, 656
+PAIR = ("nvfp4_ds_mla_write", "nvfp4_ds_mla_gather")   # the metric's two kernels
+
+
+class KernelTimer:
+    """Kernel-bound HIP events: arm(i) makes the library's next launch bind a
+    start/stop event pair of slot i to that kernel's own begin and end
+    (gcache_time_next_launch, hipExtLaunchKernel), so ms(i) is the kernel's
+    duration without the enqueue gap that events recorded around a call add
+    (a few microseconds per pair on this machine)."""
+    _hip = None
+
+    def __init__(self, gc):
+        import ctypes
+        self.gc = gc
+        self.ev = {}
+        if KernelTimer._hip is None:
+            # the HIP runtime torch and libgcache.so already share (never a second copy)
+            hip = ctypes.CDLL("libamdhip64.so.7", mode=os.RTLD_NOLOAD | os.RTLD_NOW)
+            hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+            hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventCreate.restype = hip.hipEventElapsedTime.restype = ctypes.c_int
+            KernelTimer._hip = hip
+
+    def _pair(self, i):
+        import ctypes
+        if i not in self.ev:
+            pair = []
+            for _ in range(2):
+                e = ctypes.c_void_p()
+                rc = KernelTimer._hip.hipEventCreate(ctypes.byref(e))
+                if rc != 0:
+                    raise RuntimeError(f"hipEventCreate failed ({rc})")
+                pair.append(e.value)
+            self.ev[i] = tuple(pair)
+        return self.ev[i]
+
+    def arm(self, i):
+        self.gc.time_next_launch(*self._pair(i))
+
+    def ms(self, i):
+        import ctypes
+        t = ctypes.c_float()
+        a, b = self.ev[i]
+        rc = KernelTimer._hip.hipEventElapsedTime(ctypes.byref(t), ctypes.c_void_p(a), ctypes.c_void_p(b))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(t.value)
 
 
 def parse():
@@ -189,47 +239,47 @@ def main():
         ops = [o for o in ops if o[0] in keep]
     step_bytes = sum(o[1] for o in ops)
 
-    def step(events=None, only=None):
-        for i, (_, _, _, fn) in enumerate(ops):
-            rec = events is not None and (only is None or i == only)
-            if rec:
-                events[i][0].record()
-            fn()
-            if rec:
-                events[i][1].record()
+    pair = [i for i, o in enumerate(ops) if o[0] in PAIR]
 
-    def new_events():
-        return [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in ops]
-                for _ in range(args.steps)]
+    def step(timer=None, timed=()):
+        """One pass of the ops; the kernels of the ops in `timed` carry
+        kernel-bound HIP events of `timer` (gcache_time_next_launch)."""
+        for i, (_, _, _, fn) in enumerate(ops):
+            if i in timed:
+                timer.arm(i)
+            fn()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    # ---- per-kernel pass (not the timed region): K steps with HIP events
-    # around every kernel on the launch stream.  An event pair adds a gap of a
-    # few microseconds around its kernel, so these figures come from a pass of
-    # their own and the timed region below records events around the roofline
-    # kernel only.
-    ev_all = new_events()
-    for k in range(args.steps):
-        step(ev_all[k])
-    torch.cuda.synchronize()
-    kern_ms = {name: float(np.mean([ev_all[k][i][0].elapsed_time(ev_all[k][i][1]) for k in range(args.steps)]))
-               for i, (name, _, _, _) in enumerate(ops)}
-    dom_i = max(range(len(ops)), key=lambda i: kern_ms[ops[i][0]])
+    # ---- per-kernel pass (not the timed region): K steps with every kernel's
+    # own begin and end bound to HIP events on its launch stream
+    kern = {i: [] for i in range(len(ops))}
+    kt = KernelTimer(gc)
+    for _ in range(args.steps):
+        step(kt, timed=range(len(ops)))
+        torch.cuda.synchronize()
+        for i in range(len(ops)):
+            kern[i].append(kt.ms(i))
+    kern_ms = {ops[i][0]: float(np.mean(v)) for i, v in kern.items()}
 
-    # ---- timed region: exactly K steps; HIP events around the dominant
-    # kernel only (its duration, measured live, sets roofline.achieved)
-    ev = new_events()
+    # ---- timed region: exactly K steps of the whole pass; the two NVFP4
+    # DS-MLA kernels (the metric's write and gather) carry kernel-bound HIP
+    # events, read after the region
+    live = {i: [] for i in pair}
+    timers = [KernelTimer(gc) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for k in range(args.steps):
-        step(ev[k], only=dom_i)
+        step(timers[k], timed=pair)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
+    for k in range(args.steps):
+        for i in pair:
+            live[i].append(timers[k].ms(i))
     ms_per_step = wall * 1e3 / args.steps
-    dom_ms = float(np.mean([ev[k][dom_i][0].elapsed_time(ev[k][dom_i][1]) for k in range(args.steps)]))
+    live_ms = {ops[i][0]: float(np.mean(v)) for i, v in live.items()}
 
     kernels = {}
     for name, nbytes, units, _ in ops:
@@ -268,28 +318,43 @@ def main():
                              "algorithmic_bytes": nbytes, "traffic": traffic_for(name)}
                       for name, nbytes, _, _ in ops}
 
-    dom = ops[dom_i]
-    achieved = dom[1] / (dom_ms * 1e6)
-    roofline = {"kernel": dom[0], "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "ms": round(dom_ms, 5),
-                "traffic": traffic_for(dom[0])}
+    def live_roofline(name):
+        nbytes = next(o[1] for o in ops if o[0] == name)
+        achieved = nbytes / (live_ms[name] * 1e6)
+        return {"kernel": name, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "ms": round(live_ms[name], 5),
+                "algorithmic_bytes": nbytes, "traffic": traffic_for(name)}
+
+    roofline = live_roofline("nvfp4_ds_mla_gather")
+    roofline_write = live_roofline("nvfp4_ds_mla_write")
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_budget_s, w3, g3, w4, g4, w5, g5)
 
-    value = step_bytes / (ms_per_step * 1e6)
+    pair_bytes = sum(ops[i][1] for i in pair)
+    pair_ms = sum(live_ms[ops[i][0]] for i in pair)
+    value = pair_bytes / (pair_ms * 1e6)
+    step_value = step_bytes / (ms_per_step * 1e6)
     out = {
         "metric": "effective HBM GB/s (% of peak) for NVFP4 DS-MLA cache write and gather-upconvert",
         "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16->e2m1/e4m3 (u8) and back", "data": "synthetic (seeded, see synth/)",
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
-        "config": {"workload": "prefill-context pass: nvfp4_ds_mla write 524288 tok + gather 16 req "
-                               f"({g3.total_tokens} rows); fp8_ds_mla write 1048576 tok + gather 32 req "
-                               f"({g4.total_tokens} rows); per-head nvfp4 write 8192 tok x 8 heads x 128 "
-                               f"+ gather {g5.total_tokens} rows",
+        "config": {"workload": f"nvfp4_ds_mla pre-fill write ({w3.num_tokens} tokens into {w3.num_blocks} x "
+                               f"{w3.block_size} x 352 B) + prefill gather-upconvert ({len(g3.workspace_starts)} "
+                               f"requests from seq_starts, {g3.total_tokens} rows), each timed by its own kernel "
+                               "events inside a pass of all six ops of the path",
+                   "value_bytes": pair_bytes, "value_ms": round(pair_ms, 5),
+                   "step": "nvfp4_ds_mla write 524288 tok + gather 16 req; fp8_ds_mla write 1048576 tok + "
+                           f"gather 32 req ({g4.total_tokens} rows); per-head nvfp4 write 8192 tok x 8 heads x "
+                           f"128 + gather {g5.total_tokens} rows",
                    "step_bytes": step_bytes, "ops": [o[0] for o in ops], "device": dname},
+        "step_throughput": {"value": round(step_value, 1), "unit": "GB/s",
+                            "frac_of_hbm_peak": round(step_value / HBM_PEAK_GBS, 4),
+                            "what": "algorithmic bytes of all six ops / wall time per step over the timed region"},
         "kernels": kernels,
         "roofline": roofline,
+        "roofline_write": roofline_write,
         "roofline_by_op": roofline_by_op,
         "cpu_baseline": cpu,
         "extras": extras,
@@ -402,6 +467,10 @@ def measure_extras(torch, gc, g3, steps, dev_arr, cache3, perhead):
             scale_token_stride=H * fd, scale_head_stride=fd, side_stride=bs5 * H * fd,
             block_stride=2 * bs5 * H * fd)}
     cache5 = torch.zeros((w5.num_blocks, 2, bs5, H, fd), dtype=torch.uint8, device="cuda")
+    gp5 = synth.perhead_prefill_gather()
+    ko_p = torch.empty((gp5.total_tokens, H, hs), dtype=torch.bfloat16, device="cuda")
+    vo_p = torch.empty_like(ko_p)
+    bt_p, ws_p, ss_p = dev_arr(gp5.block_table), dev_arr(gp5.workspace_starts), dev_arr(gp5.seq_starts)
     for lname, L in layouts.items():
         what = ("the default split layout" if lname == "split_rows" else
                 f"each (token, head) cache row laid out as [{hs // 2} data | {hs // 16} scale] bytes")
@@ -414,6 +483,12 @@ def measure_extras(torch, gc, g3, steps, dev_arr, cache3, perhead):
                                                                    layout=L), steps)
         out[f"perhead_gather_{lname}"] = _extra(ms, kv_gather_bytes(g5, H, hs), g5.total_tokens,
                                                 f"the per-head gather workload, {what}")
+        ms = device_ms(torch, lambda: gc.gather_upconvert_nvfp4_kv(cache5, ko_p, vo_p, bt_p, ws_p, d["ks5"], d["vs5"],
+                                                                   seq_starts=ss_p, layout=L), steps)
+        out[f"perhead_gather_prefill_walk_{lname}"] = _extra(
+            ms, kv_gather_bytes(gp5, H, hs), gp5.total_tokens,
+            f"per-head gather on a prefill walk: {len(gp5.workspace_starts)} requests, L ~ U[512, 6144] from "
+            f"seq_starts ~ U[0, L/2], {gp5.total_tokens} rows over the per-head cache's {w5.num_blocks} blocks, {what}")
     del cache5
 
     w2 = synth.decode_batch_write()
@@ -675,12 +750,18 @@ def write_stats(prof_dir, bench_json, extras=False):
             for k, v in b["extras"].items():
                 md.append(f"| {k} | {v['ms']:.5f} | {v['GB_per_s']:.0f} | {100 * v['frac_of_hbm_peak']:.1f} |")
         else:
-            md += ["", f"Same-build HIP-event averages from `python bench.py` (per-kernel pass of {b['steps']} "
-                   f"steps; whole step over the {b['steps']} timed steps {b['value']} GB/s, "
-                   f"{100 * b['frac_of_hbm_peak']:.1f} % of 8 TB/s):", "",
+            md += ["", "Same-build figures from an unprofiled `python bench.py` run (inside the profiled run "
+                   "the same events read longer than rocprofv3's own durations), all from "
+                   "HIP events bound to each kernel's own begin and end (gcache_time_next_launch), so they "
+                   f"measure what rocprofv3 measures. Per-kernel pass of {b['steps']} steps:", "",
                    "| Kernel op | ms | GB/s | % of 8 TB/s |", "|---|---|---|---|"]
             for k, v in b["kernels"].items():
                 md.append(f"| {k} | {v['ms']:.5f} | {v['GB_per_s']:.0f} | {100 * v['frac_of_hbm_peak']:.1f} |")
+            md += ["", f"Inside the {b['steps']} timed steps: nvfp4_ds_mla write {b['roofline_write']['ms']:.5f} ms "
+                   f"({100 * b['roofline_write']['frac']:.1f} %), gather {b['roofline']['ms']:.5f} ms "
+                   f"({100 * b['roofline']['frac']:.1f} %); the metric's value (the pair's bytes over the pair's "
+                   f"kernel time) {b['value']} GB/s, {100 * b['frac_of_hbm_peak']:.1f} % of 8 TB/s; whole six-op step "
+                   f"{b['step_throughput']['value']} GB/s."]
     name = "extras_kernels_stats.md" if extras else "prefill_pass_all_kernels_stats.md"
     with open(os.path.join(ROOT, "profiles", name), "w") as f:
         f.write("\n".join(md) + "\n")
@@ -916,18 +997,25 @@ def cpu_baseline(budget_s, w3, g3, w4, g4, w5, g5):
             nbytes = nbytes_of(n)
             res[name] = {"units": n, "s_1_thread": round(sec1, 3), f"s_{threads}_threads": round(secm, 3),
                          "GB_per_s_1_thread": round(nbytes / sec1 / 1e9, 4),
-                         "GB_per_s": round(nbytes / secm / 1e9, 4)}
+                         "GB_per_s": round(nbytes / secm / 1e9, 4), "bytes": nbytes}
             tot_bytes += nbytes
             tot_1 += sec1
             tot_mt += secm
             desc.append(f"{name} {n}/{avail}")
-    return {"value": round(tot_bytes / tot_mt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": "first units of each op's full workload (" + ", ".join(desc) + "); write samples "
-                      "take the first tokens, gather samples the first workspace rows; the C oracle (gcc -O2) "
-                      f"unchanged, run on {threads} host threads (writes split by token ranges, gathers by "
-                      f"runs of whole requests): {tot_mt:.1f} s wall; the same samples on one thread took "
-                      f"{tot_1:.1f} s",
-            "value_1_thread": round(tot_bytes / tot_1 / 1e9, 4),
+    pb = sum(res[n]["bytes"] for n in PAIR)
+    pm = sum(res[n][f"s_{threads}_threads"] for n in PAIR)
+    p1 = sum(res[n]["s_1_thread"] for n in PAIR)
+    return {"value": round(pb / pm / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": "the metric's pair: the first tokens of the nvfp4_ds_mla pre-fill write and the first "
+                      "workspace rows of its prefill gather (" + ", ".join(d for d in desc if d.split()[0] in PAIR)
+                      + "), the C oracle (gcc -O2) unchanged, on " f"{threads} host threads (writes split by "
+                      f"token ranges, gathers by runs of whole requests): {pm:.1f} s wall ({p1:.1f} s on one "
+                      "thread); value = their algorithmic bytes over that time.  The other four ops' samples ("
+                      + ", ".join(d for d in desc if d.split()[0] not in PAIR) + ") are in per_op and in "
+                      f"value_all_ops ({tot_mt:.1f} s wall for all six)",
+            "value_1_thread": round(pb / p1 / 1e9, 4),
+            "value_all_ops": round(tot_bytes / tot_mt / 1e9, 4),
+            "value_all_ops_1_thread": round(tot_bytes / tot_1 / 1e9, 4),
             "per_op": res, "host_cpu": _cpu_name()}
 
 

@@ -41,6 +41,7 @@ _SIGS = {
     "gcache_entry_bytes": (_I64, [C.c_int]),
     "gcache_nvfp4_full_dim": (_I32, [_I32]),
     "gcache_status_string": (C.c_char_p, [C.c_int]),
+    "gcache_time_next_launch": (C.c_int, [_P, _P]),
     "gcache_cache_write_nvfp4_ds_mla": (C.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _I64, _I32, _I64, _I64, _P]),
     "gcache_cache_write_fp8_ds_mla": (C.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _I64, _I32, _I64, _I64, _P]),
     "gcache_cache_gather_upconvert_nvfp4_ds_mla": (C.c_int, [_P, _P, _I64, _I64, _P, _I64, _P, _P, _I32, _I64,
@@ -104,6 +105,14 @@ def _dev_tensor(t, dtype, name, device=None):
 def _stream(device, stream):
     s = torch.cuda.current_stream(device) if stream is None else stream
     return s.cuda_stream
+
+
+def time_next_launch(start_event, stop_event):
+    """Bind the next kernel that this library launches from the calling
+    thread to two HIP events (raw hipEvent_t handles as integers, or None):
+    `start_event` records when that kernel begins, `stop_event` when it ends
+    (gcache_time_next_launch)."""
+    _check(load().gcache_time_next_launch(start_event, stop_event), "time_next_launch")
 
 
 def entry_bytes(fmt):

@@ -14,6 +14,12 @@
 
 using namespace gcache;
 
+// Timing events armed by gcache_time_next_launch, per host thread.
+LaunchTiming& gcache::launch_timing() {
+    static thread_local LaunchTiming t;
+    return t;
+}
+
 namespace {
 
 constexpr int kMaxDevices = 64;
@@ -189,6 +195,11 @@ int64_t gcache_entry_bytes(gcache_format format) {
 int32_t gcache_nvfp4_full_dim(int32_t head_size) {
     if (head_size <= 0 || head_size % 16) return -1;
     return head_size / 2 + head_size / 16;
+}
+
+int gcache_time_next_launch(hipEvent_t start, hipEvent_t stop) {
+    launch_timing() = LaunchTiming{start, stop};
+    return GCACHE_OK;
 }
 
 const char* gcache_status_string(int status) {

@@ -3,6 +3,7 @@
 // fill one of these structs and call the matching launcher.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -101,6 +102,25 @@ int32_t staged_span(const KvLayout& L, int32_t num_heads, int32_t head_size);
 hipError_t launch_gather_nvfp4_kv(const KvGatherParams& p, hipStream_t s);
 hipError_t launch_convert_req_index(const SparseIndexParams& p, hipStream_t s);
 
+// Events armed by gcache_time_next_launch for the next launch on this host
+// thread (consumed by that launch).
+struct LaunchTiming {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+LaunchTiming& launch_timing();
+
+// One grid launch.  When timing events are armed, the first piece of the
+// launch takes `start` and the last piece `stop` (hipExtLaunchKernel binds
+// them to the kernel's own begin and end); otherwise a plain launch.
+inline hipError_t launch_piece(const void* kernel, int64_t blocks, int threads, void** args, hipStream_t s,
+                               bool first, bool last) {
+    LaunchTiming& t = launch_timing();
+    hipEvent_t a = first ? t.start : nullptr, b = last ? t.stop : nullptr;
+    if (!a && !b) return hipLaunchKernel(kernel, dim3((unsigned)blocks), dim3(threads), args, 0, s);
+    if (last) t = LaunchTiming{};
+    return hipExtLaunchKernel(kernel, dim3((unsigned)blocks), dim3(threads), args, 0, s, a, b, 0);
+}
+
 // Launch `waves` one-shot waves of `kernel(params, wave0)`: the kernel's
 // wave index is wave0 + blockIdx.x * kWavesPerBlock + wave_id().  Grids are
 // split into launches of at most 2^24 workgroups (far beyond any realistic
@@ -113,8 +133,8 @@ inline hipError_t launch_waves(void (*kernel)(P, int64_t), int64_t waves, hipStr
         const int64_t nb = blocks - b0 < kMaxBlocks ? blocks - b0 : kMaxBlocks;
         int64_t wave0 = b0 * kWavesPerBlock;
         void* args[] = {const_cast<P*>(&p), &wave0};
-        const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3((unsigned)nb),
-                                             dim3(kBlockThreads), args, 0, s);
+        const hipError_t e = launch_piece(reinterpret_cast<const void*>(kernel), nb, kBlockThreads, args, s,
+                                          b0 == 0, b0 + nb >= blocks);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
@@ -131,8 +151,8 @@ inline hipError_t launch_groups(void (*kernel)(P, int64_t), int64_t groups, hipS
         const int64_t nb = groups - b0 < kMaxBlocks ? groups - b0 : kMaxBlocks;
         int64_t group0 = b0;
         void* args[] = {const_cast<P*>(&p), &group0};
-        const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3((unsigned)nb),
-                                             dim3(threads), args, 0, s);
+        const hipError_t e = launch_piece(reinterpret_cast<const void*>(kernel), nb, threads, args, s, b0 == 0,
+                                          b0 + nb >= groups);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;

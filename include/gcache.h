@@ -87,6 +87,22 @@ int32_t gcache_nvfp4_full_dim(int32_t head_size);
 const char* gcache_status_string(int status);
 
 /*
+ * Measurement hook (not part of the pages' operations; for benchmarks and
+ * profilers that need a kernel's own duration).  The next kernel that an
+ * entry point of this library launches from the calling host thread binds
+ * `start` to the moment that kernel begins executing and `stop` to the
+ * moment it ends (hipExtLaunchKernel), so hipEventElapsedTime(start, stop)
+ * is the kernel's duration without the enqueue gaps that events recorded
+ * around the call include.  Both events are created and owned by the caller
+ * (timing enabled, on the device of the launch); either may be NULL.  The
+ * hook is thread-local and consumed by that one launch: a call that is
+ * rejected or launches nothing (for instance num_tokens == 0) leaves it
+ * armed for the next call, and gcache_time_next_launch(NULL, NULL) disarms
+ * it.  Always returns GCACHE_OK.
+ */
+int gcache_time_next_launch(hipEvent_t start, hipEvent_t stop);
+
+/*
  * nvfp4_ds_mla write -- [PR51724] "Implementation breakdown" item 3 and the
  * write-kernel excerpt in "Key source excerpts".
  *

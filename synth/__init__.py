@@ -214,6 +214,13 @@ def fp8_prefill_gather():
     return prefill_gather(_rng(1004, 1), "fp8-prefill-gather", 32, 512, 16384, 16384, 64, 256)
 
 
+def perhead_prefill_gather():
+    """Per-head gather on a prefill-shaped walk over the per-head cache's 4096
+    blocks of 16: 16 requests, L ~ U[512, 6144], seq_start ~ U[0, L/2], block
+    tables over a shuffle of the blocks (384 per request)."""
+    return prefill_gather(_rng(1005, 3), "perhead-prefill-gather", 16, 512, 6144, 4096, 16, 384)
+
+
 def perhead_write_gather():
     """Per-head NVFP4 K/V write: 8192 tokens, 8 KV heads of 128, K and V each
     N(0,1) x a per-head magnitude ~ U[0.1, 10] (drawn separately for K and V);

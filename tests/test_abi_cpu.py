@@ -37,9 +37,14 @@ def test_every_declared_symbol_is_exported(lib):
         "gcache_cache_gather_bf16", "gcache_context_chunk_plan", "gcache_context_chunk",
         "gcache_convert_req_index_to_global_index",
         "gcache_nvfp4_kv_split_layout", "gcache_nvfp4_kv_split_layout_hnd", "gcache_reshape_and_cache_nvfp4",
-        "gcache_gather_upconvert_nvfp4_kv"]), names
+        "gcache_gather_upconvert_nvfp4_kv", "gcache_time_next_launch"]), names
     for n in names:
         assert hasattr(lib, n), f"{n} not exported by libgcache.so"
+
+
+def test_timing_hook_is_host_only(lib):
+    """Arming and disarming the kernel timing hook touches no device."""
+    assert lib.gcache_time_next_launch(None, None) == 0
 
 
 def test_host_helpers(lib):

@@ -146,6 +146,44 @@ def test_rounding_order_hand_vectors(g, orc):
             assert [f"{b:#06x}" for b in k] == h["dequant_bits"], h["name"]
 
 
+def test_kernel_timing_hook(g, orc):
+    """gcache_time_next_launch binds the next launch's own begin and end to
+    two events: the kernel still computes the same bytes, the elapsed time is
+    positive and no longer than events recorded around the call, a rejected
+    call leaves the hook armed, and the launch after the timed one is plain."""
+    import ctypes
+    import os
+    hip = ctypes.CDLL("libamdhip64.so.7", mode=os.RTLD_NOLOAD | os.RTLD_NOW)
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    ev = []
+    for _ in range(2):
+        e = ctypes.c_void_p()
+        assert hip.hipEventCreate(ctypes.byref(e)) == 0
+        ev.append(e.value)
+    w = synth.decode_batch_write()
+    eb, gwrite, _ = _ds_pair("nvfp4")
+    want = np.full(w.num_blocks * w.block_size * eb, 0xA5, np.uint8)
+    orc.write_nvfp4_ds_mla(w.kv_c, w.k_pe, want, w.slot_mapping, w.num_blocks, w.block_size)
+    kv, pe, sl = dev(w.kv_c), dev(w.k_pe), dev(w.slot_mapping)
+    flat = filled_cache((w.num_blocks * w.block_size * eb,), 0xA5)
+    cache = flat.view(w.num_blocks, w.block_size, eb)
+    g.time_next_launch(ev[0], ev[1])
+    odd_stride = torch.zeros((w.kv_c.shape[0], 513), dtype=torch.bfloat16, device="cuda")[:, :512]
+    with pytest.raises(g.GcacheError):                       # rejected (row stride 513): hook kept
+        gwrite(odd_stride, pe, cache, sl)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    gwrite(kv, pe, cache, sl)                                # the timed launch
+    b.record()
+    gwrite(kv, pe, cache, sl)                                # plain launch: the events keep the first
+    torch.cuda.synchronize()
+    assert_same(host(flat), want, "write under the timing hook")
+    t = ctypes.c_float()
+    assert hip.hipEventElapsedTime(ctypes.byref(t), ctypes.c_void_p(ev[0]), ctypes.c_void_p(ev[1])) == 0
+    assert 0.0 < t.value <= a.elapsed_time(b), (t.value, a.elapsed_time(b))
+
+
 @pytest.mark.parametrize("fmt", ["nvfp4", "fp8"])
 def test_decode_batch_write(g, orc, fmt):
     w = synth.decode_batch_write()
@@ -583,6 +621,77 @@ def test_perhead_layouts(g, orc, variant):
         big2[:, :, :hs] = value
         vd = dev(big2)[:, :, :hs]
     run_kv(orc, g, key, value, slots, nb, bs, L_orc, L_gpu, ks, vs, kd, vd, out_hnd=(variant == "hnd"))
+
+
+def _prefill_requests(rng, B, nb, bs, long_len, empties):
+    """B requests over a shuffle of the nb blocks: lengths U[1, 520] plus one
+    request of long_len positions, gather starts U[0, L] (a start at L makes
+    the request empty) with the requests in `empties` forced empty and a few
+    starts inside the first block; workspace_starts = exclusive cumsum."""
+    L = rng.integers(1, 521, size=B).astype(np.int64)
+    L[B // 2] = long_len
+    s = rng.integers(0, L + 1).astype(np.int64)
+    s[empties] = L[empties]
+    s[1], s[2] = 0, min(5, int(L[2]))
+    nblk = -(-L // bs)
+    assert nblk.sum() <= nb
+    perm = rng.permutation(nb).astype(np.int32)
+    bt = np.full((B, int(nblk.max()) + 2), -1, np.int32)
+    pos = 0
+    for b in range(B):
+        bt[b, :nblk[b]] = perm[pos:pos + nblk[b]]
+        pos += nblk[b]
+    rows = L - s
+    ws = np.concatenate([[0], np.cumsum(rows)[:-1]]).astype(np.int32)
+    return synth.GatherCase("prefill walk", bt, ws, s.astype(np.int32), int(rows.sum()), nb, bs, L)
+
+
+@pytest.mark.parametrize("layout", ["nhd-split", "hnd-split", "rows"])
+def test_perhead_prefill_walks(g, orc, layout):
+    """The per-head gather on prefill-shaped walks (multi-row requests read
+    from seq_starts, empty requests, one long request spanning many blocks):
+    48 requests, about 8k rows, 8 heads of 128, over a cache whose every slot
+    was written by the per-head write; NHD and HND split layouts and
+    [data | scale] rows (the staged kernels).  Every byte and output bit
+    against the oracle, with and without seq_starts."""
+    rng = np.random.default_rng({"nhd-split": 61, "hnd-split": 62, "rows": 63}[layout])
+    H, hs, bs, nb, B = 8, 128, 16, 1280, 48
+    fd = hs // 2 + hs // 16
+    T = nb * bs
+    key, value, _ = _kv_case(rng, T, H, hs, nb, bs, 0)
+    slots = rng.permutation(T).astype(np.int64)
+    ks, vs = synth.global_scale(key), synth.global_scale(value)
+    if layout == "rows":
+        kw = dict(data_offset=0, data_token_stride=H * fd, data_head_stride=fd, scale_offset=hs // 2,
+                  scale_token_stride=H * fd, scale_head_stride=fd, side_stride=bs * H * fd,
+                  block_stride=2 * bs * H * fd)
+        L_orc, L_gpu = orc.KvLayout(**kw), g.NvFp4KvLayout(**kw)
+    else:
+        L_orc = orc.kv_layout_split(bs, H, hs, hnd=layout == "hnd-split")
+        L_gpu = g.nvfp4_kv_split_layout(bs, H, hs, hnd=layout == "hnd-split")
+    size = nb * L_orc.block_stride
+    want = np.full(size, 0xA5, np.uint8)
+    orc.reshape_and_cache_nvfp4(key, value, want, slots, nb, bs, L_orc, ks, vs)
+    flat = filled_cache((size,), 0xA5)
+    cache5 = torch.as_strided(flat, (nb, 2, bs, H, fd), (L_orc.block_stride, L_orc.side_stride, H * fd, fd, 1))
+    ks_d = torch.tensor([ks], dtype=torch.float32, device="cuda")
+    vs_d = torch.tensor([vs], dtype=torch.float32, device="cuda")
+    g.reshape_and_cache_nvfp4(dev(key), dev(value), cache5, dev(slots), ks_d, vs_d, layout=L_gpu)
+    torch.cuda.synchronize()
+    assert_same(host(flat), want, f"per-head write ({layout})")
+    gc_ = _prefill_requests(rng, B, nb, bs, 3000, [3, 17, 40])
+    assert 5000 < gc_.total_tokens < 12000
+    for ss in (gc_.seq_starts, None):
+        ok, ov = orc.gather_upconvert_nvfp4_kv(want, gc_.total_tokens, gc_.block_table, gc_.workspace_starts,
+                                               ss, H, hs, nb, bs, L_orc, ks, vs)
+        ko = torch.full((gc_.total_tokens, H, hs), 7.0, dtype=torch.bfloat16, device="cuda")
+        vo = torch.full((gc_.total_tokens, H, hs), 7.0, dtype=torch.bfloat16, device="cuda")
+        g.gather_upconvert_nvfp4_kv(cache5, ko, vo, dev(gc_.block_table), dev(gc_.workspace_starts), ks_d, vs_d,
+                                    seq_starts=None if ss is None else dev(ss), layout=L_gpu)
+        torch.cuda.synchronize()
+        what = f"per-head prefill gather ({layout}, {'with' if ss is not None else 'without'} seq_starts)"
+        assert_same(host(ko), ok, what + " K")
+        assert_same(host(vo), ov, what + " V")
 
 
 def test_perhead_out_of_range_metadata(g, orc):
