@@ -173,7 +173,8 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
-              "(the path is token-parallel; see the design notes for how it shards).", file=sys.stderr)
+              "(every op is token-parallel with no exchange between tokens, so one GPU's share at its real "
+              "shape is what it times).", file=sys.stderr)
         sys.exit(2)
     import torch
     import gather_concat_cache_amd as gc

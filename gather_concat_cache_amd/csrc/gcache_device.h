@@ -1,8 +1,9 @@
 // gcache_device.h -- device helpers shared by the gfx950 kernels.
 //
-// Conversions use the gfx950 hardware converters.  Each one was checked
-// exhaustively against round-to-nearest-even over every non-NaN binary32
-// input (scale operand 1.0; see the design notes for the sweep):
+// Conversions use the gfx950 hardware converters.  Each one is checked
+// exhaustively against the CPU reference's round-to-nearest-even encoders
+// over every non-NaN binary32 input (scale operand 1.0) by the GPU test
+// tests/test_gpu_converters.py, which runs these helpers:
 //   v_cvt_scalef32_pk_fp4_f32  e2m1, RN-even, saturating at +-6, sign kept
 //                              (-0 and tiny negatives give 0x8); the first
 //                              operand lands in the low nibble.

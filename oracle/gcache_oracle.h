@@ -23,7 +23,7 @@
  * IEEE-754 binary32 round-to-nearest-even.
  *
  * Readings taken where the pages are silent are marked READING in the .c
- * file; every one of them is listed in the design notes of the repository.
+ * file.
  *
  * Parity status: every function below is pinned by the CPU test suite
  * (exhaustive codec sweeps against an independent bit-level encoder,
