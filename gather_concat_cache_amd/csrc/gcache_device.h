@@ -111,9 +111,17 @@ __device__ __forceinline__ uint32_t ld_stream4(const void* p) {
 __device__ __forceinline__ uint32_t ld_stream1(const void* p) {
     return __builtin_nontemporal_load(static_cast<const uint8_t*>(p));
 }
+// The 16-byte store every kernel writes its outputs with also carries the
+// system-scope bits (sc0 sc1): the piece is written through to memory
+// instead of staying dirty in L2, so a kernel leaves no write-back for the
+// next one on the stream to absorb (measured in the six-op pass: the writes
+// and the fp8 gather 1-2 % faster, the metric's pair +1-1.5 %).  No builtin
+// sets these bits on a global store, hence one global_store_dwordx4 in
+// inline asm (a vector store); the s_nop keeps two wait states before a
+// VALU may overwrite the store's data registers.
 __device__ __forceinline__ void st_stream16(void* p, uint4 v) {
     const u32x4 w = {v.x, v.y, v.z, v.w};
-    __builtin_nontemporal_store(w, static_cast<u32x4*>(p));
+    asm volatile("global_store_dwordx4 %0, %1, off sc0 sc1 nt\n\ts_nop 1" : : "v"(p), "v"(w) : "memory");
 }
 __device__ __forceinline__ void st_stream8(void* p, uint2 v) {
     const u32x2 w = {v.x, v.y};
