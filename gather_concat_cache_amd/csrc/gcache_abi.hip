@@ -426,7 +426,7 @@ int gcache_reshape_and_cache_nvfp4(const void* key, const void* value, int64_t k
     p.L = to_layout(layout);
     p.gscale[0] = k_scale;
     p.gscale[1] = v_scale;
-    p.span = staged_span(p.L, num_heads, head_size);
+    p.st = staged_layout(p.L, num_heads, head_size);
     return launched(launch_reshape_and_cache_nvfp4(p, stream));
 }
 
@@ -473,7 +473,7 @@ int gcache_gather_upconvert_nvfp4_kv(const void* kv_cache, void* key_out, void* 
     p.L = to_layout(layout);
     p.gscale[0] = k_scale;
     p.gscale[1] = v_scale;
-    p.span = staged_span(p.L, num_heads, head_size);
+    p.st = staged_layout(p.L, num_heads, head_size);
     return launched(launch_gather_nvfp4_kv(p, stream));
 }
 

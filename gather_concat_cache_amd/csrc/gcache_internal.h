@@ -43,6 +43,18 @@ struct KvLayout {                // mirrors gcache_nvfp4_kv_layout (bytes)
     int64_t side_stride, block_stride;
 };
 
+// Staging of the per-head kernels: when the layout keeps a (token, side)'s
+// bytes in at most two contiguous, 16-byte aligned runs, the kernels move
+// them as 16-byte pieces through an LDS image of `span` bytes per side:
+// image bytes [0, run0) are run 0 (at data_offset + off * data_token_stride),
+// [run0, span) are run 1 (at scale_offset + off * scale_token_stride).
+// Inside the image, head h's data starts at h * data_head and its scales at
+// scale_off + h * scale_head.  span == 0: the direct (unstaged) kernels.
+struct KvStage {
+    int32_t span, run0;
+    int32_t data_head, scale_off, scale_head;
+};
+
 struct KvWriteParams {
     const uint16_t* src[2];      // key, value: bf16 [T, H, hs]
     int64_t token_stride[2], head_stride[2];  // elements
@@ -55,7 +67,7 @@ struct KvWriteParams {
     BlockDiv div;
     KvLayout L;
     const float* gscale[2];      // k_scale, v_scale (device scalars)
-    int32_t span;                // > 0: staged kernels, contiguous (token, side) run bytes
+    KvStage st;                  // st.span > 0: staged kernels
 };
 
 struct KvGatherParams {
@@ -74,7 +86,7 @@ struct KvGatherParams {
     BlockDiv div;
     KvLayout L;
     const float* gscale[2];
-    int32_t span;                // > 0: staged kernels, contiguous (token, side) run bytes
+    KvStage st;                  // st.span > 0: staged kernels
 };
 
 struct SparseIndexParams {
@@ -98,7 +110,7 @@ hipError_t launch_gather_nvfp4_ds_mla(const DsMlaGatherParams& p, hipStream_t s)
 hipError_t launch_gather_fp8_ds_mla(const DsMlaGatherParams& p, hipStream_t s);
 hipError_t launch_gather_bf16(const DsMlaGatherParams& p, hipStream_t s);
 hipError_t launch_reshape_and_cache_nvfp4(const KvWriteParams& p, hipStream_t s);
-int32_t staged_span(const KvLayout& L, int32_t num_heads, int32_t head_size);
+KvStage staged_layout(const KvLayout& L, int32_t num_heads, int32_t head_size);
 hipError_t launch_gather_nvfp4_kv(const KvGatherParams& p, hipStream_t s);
 hipError_t launch_convert_req_index(const SparseIndexParams& p, hipStream_t s);
 

@@ -9,10 +9,13 @@
 //            side (32 B in, 8 B data + 1 scale byte out).  With 8 heads of
 //            128 values a side is exactly 64 blocks, so both sides' loads
 //            (64 B per lane) are in flight before any is used.
-//   staged : when each (token, side) of the layout is one contiguous run of
-//            [data | scales] rows (the interleaved-row arrangement), the
-//            write assembles the runs in LDS and stores 16-byte pieces, and
-//            the gather loads the runs as 16-byte pieces into LDS first.
+//   staged : when each (token, side) of the layout is at most two
+//            contiguous, 16-byte aligned runs -- the token's data of all
+//            heads and its scales of all heads (the NHD split layout), or
+//            one run of [data | scales] rows (the interleaved-row
+//            arrangement) -- the write assembles the runs in LDS and stores
+//            16-byte pieces, and the gather loads them as 16-byte pieces
+//            into LDS first.
 //   gather : one workspace row per one-shot wave (both sides, all heads);
 //            the row's cache address is resolved once (wave-uniform search
 //            over workspace_starts, one block-table load), then one lane per
@@ -35,15 +38,19 @@ __device__ __forceinline__ void split_pow2(int v, int shift, int n, int& q, int&
 constexpr int kKvItemsPerLane = 2;   // blocks in flight per lane and pass
 constexpr int kKvMaxSpan = 2048;     // largest staged (token, side) run, bytes
 
-// Cache byte offset of byte b of a staged (token, side) run.
-__device__ __forceinline__ int64_t kv_run_offset(const KvLayout& L, int64_t blk, int side, int64_t off, int b) {
-    return blk * L.block_stride + side * L.side_stride + L.data_offset + off * L.data_token_stride + b;
+// Cache byte offset of byte b of a staged (token, side) image: image bytes
+// [0, run0) are run 0 (the data run), the rest run 1 (the scale run).
+__device__ __forceinline__ int64_t kv_run_offset(const KvLayout& L, const KvStage& st, int64_t blk, int side,
+                                                 int64_t off, int b) {
+    const int64_t base = blk * L.block_stride + side * L.side_stride;
+    return b < st.run0 ? base + L.data_offset + off * L.data_token_stride + b
+                       : base + L.scale_offset + off * L.scale_token_stride + (b - st.run0);
 }
 
-// STAGED: the layout keeps each (token, side) in one contiguous, 16-byte
-// aligned run of p.span bytes (see staged_span).  The wave then assembles
-// the token's two runs in LDS and writes them as 16-byte pieces instead of
-// 8-byte code runs and single scale bytes that each cover part of a line.
+// STAGED: the layout keeps each (token, side) in at most two contiguous,
+// 16-byte aligned runs (see staged_layout).  The wave then assembles the
+// token's images in LDS and writes them as 16-byte pieces instead of 8-byte
+// code runs and single scale bytes that each cover part of a line.
 template <bool STAGED>
 __global__ __launch_bounds__(kBlockThreads) void k_reshape_and_cache_nvfp4(KvWriteParams p, int64_t wave0) {
     __shared__ __align__(16) uint8_t s_img[STAGED ? kWavesPerBlock : 1][STAGED ? 2 * kKvMaxSpan : 16];
@@ -112,10 +119,10 @@ __global__ __launch_bounds__(kBlockThreads) void k_reshape_and_cache_nvfp4(KvWri
                 q1 = put_e2m1x2<1>(q1, x[10] * inv, x[11] * inv);
                 q1 = put_e2m1x2<2>(q1, x[12] * inv, x[13] * inv);
                 q1 = put_e2m1x2<3>(q1, x[14] * inv, x[15] * inv);
-                if (STAGED) {                            // image of the token's two runs
-                    uint8_t* img = s_img[wave_id()] + side * p.span;
-                    *reinterpret_cast<uint2*>(img + h * p.L.data_head_stride + 8 * j) = make_uint2(q0, q1);
-                    img[p.L.scale_offset - p.L.data_offset + h * p.L.scale_head_stride + j] = (uint8_t)sf;
+                if (STAGED) {                            // image of the token's (token, side) runs
+                    uint8_t* img = s_img[wave_id()] + side * p.st.span;
+                    *reinterpret_cast<uint2*>(img + h * p.st.data_head + 8 * j) = make_uint2(q0, q1);
+                    img[p.st.scale_off + h * p.st.scale_head + j] = (uint8_t)sf;
                     continue;
                 }
                 uint8_t* base_ptr = p.cache + blk * p.L.block_stride + side * p.L.side_stride;
@@ -132,12 +139,12 @@ __global__ __launch_bounds__(kBlockThreads) void k_reshape_and_cache_nvfp4(KvWri
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             const uint8_t* img = s_img[wave_id()];
-            const int pieces = p.span >> 4;              // per side
+            const int pieces = p.st.span >> 4;           // per side
             for (int q = lane; q < 2 * pieces; q += kWave) {
                 const int side = q >= pieces;
                 const int k = q - side * pieces;
-                st_stream16(p.cache + kv_run_offset(p.L, blk, side, off, 16 * k),
-                            *reinterpret_cast<const uint4*>(img + side * p.span + 16 * k));
+                st_stream16(p.cache + kv_run_offset(p.L, p.st, blk, side, off, 16 * k),
+                            *reinterpret_cast<const uint4*>(img + side * p.st.span + 16 * k));
             }
         }
     }
@@ -145,10 +152,9 @@ __global__ __launch_bounds__(kBlockThreads) void k_reshape_and_cache_nvfp4(KvWri
 
 constexpr int kKvGatherItems = 4;   // 8-value chunks per lane and pass
 
-// STAGED: as for the write, each (token, side) is one contiguous run; the
-// wave loads the row's two runs as 16-byte pieces into LDS and converts
-// from there instead of 4-byte code and 1-byte scale loads spread over the
-// interleaved rows.
+// STAGED: as for the write, each (token, side) is at most two contiguous
+// runs; the wave loads the row's runs as 16-byte pieces into LDS and
+// converts from there instead of 4-byte code and 1-byte scale loads.
 template <bool STAGED>
 __global__ __launch_bounds__(kBlockThreads) void k_gather_nvfp4_kv(KvGatherParams p, int64_t wave0) {
     __shared__ __align__(16) uint8_t s_img[STAGED ? kWavesPerBlock : 1][STAGED ? 2 * kKvMaxSpan : 16];
@@ -185,14 +191,14 @@ __global__ __launch_bounds__(kBlockThreads) void k_gather_nvfp4_kv(KvGatherParam
     }
     const float gs_k = *p.gscale[0], gs_v = *p.gscale[1];
 
-    if (STAGED && blk >= 0) {                            // the row's two runs -> LDS
+    if (STAGED && blk >= 0) {                            // the row's runs -> LDS
         uint8_t* img = s_img[wave_id()];
-        const int pieces = p.span >> 4;
+        const int pieces = p.st.span >> 4;
         for (int q = lane; q < 2 * pieces; q += kWave) {
             const int side = q >= pieces;
             const int k = q - side * pieces;
-            *reinterpret_cast<uint4*>(img + side * p.span + 16 * k) =
-                ld_stream16(p.cache + kv_run_offset(p.L, blk, side, off, 16 * k));
+            *reinterpret_cast<uint4*>(img + side * p.st.span + 16 * k) =
+                ld_stream16(p.cache + kv_run_offset(p.L, p.st, blk, side, off, 16 * k));
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
@@ -209,9 +215,9 @@ __global__ __launch_bounds__(kBlockThreads) void k_gather_nvfp4_kv(KvGatherParam
                 int h, i;
                 split_pow2(it - side * nchunk, p.cph_shift, cph, h, i);   // values 8i..8i+7 of head h
                 if (STAGED) {
-                    const uint8_t* img = s_img[wave_id()] + side * p.span;
-                    nib[u] = *reinterpret_cast<const uint32_t*>(img + h * p.L.data_head_stride + 4 * i);
-                    sfb[u] = img[p.L.scale_offset - p.L.data_offset + h * p.L.scale_head_stride + (i >> 1)];
+                    const uint8_t* img = s_img[wave_id()] + side * p.st.span;
+                    nib[u] = *reinterpret_cast<const uint32_t*>(img + h * p.st.data_head + 4 * i);
+                    sfb[u] = img[p.st.scale_off + h * p.st.scale_head + (i >> 1)];
                     continue;
                 }
                 const uint8_t* sb = p.cache + blk * p.L.block_stride + side * p.L.side_stride;
@@ -244,27 +250,35 @@ __global__ __launch_bounds__(kBlockThreads) void k_gather_nvfp4_kv(KvGatherParam
 }
 
 hipError_t launch_reshape_and_cache_nvfp4(const KvWriteParams& p, hipStream_t s) {
-    return p.span ? launch_waves(k_reshape_and_cache_nvfp4<true>, p.num_tokens, s, p)
-                  : launch_waves(k_reshape_and_cache_nvfp4<false>, p.num_tokens, s, p);
+    return p.st.span ? launch_waves(k_reshape_and_cache_nvfp4<true>, p.num_tokens, s, p)
+                     : launch_waves(k_reshape_and_cache_nvfp4<false>, p.num_tokens, s, p);
 }
 hipError_t launch_gather_nvfp4_kv(const KvGatherParams& p, hipStream_t s) {
-    return p.span ? launch_waves(k_gather_nvfp4_kv<true>, p.total, s, p)
-                  : launch_waves(k_gather_nvfp4_kv<false>, p.total, s, p);
+    return p.st.span ? launch_waves(k_gather_nvfp4_kv<true>, p.total, s, p)
+                     : launch_waves(k_gather_nvfp4_kv<false>, p.total, s, p);
 }
 
-// The staged kernels apply when each (token, side) of the layout is one
-// contiguous, 16-byte aligned run: rows of [data | scales], head after head
-// (interleaved rows), at most kKvMaxSpan bytes.  Returns that run's length,
-// or 0 (the direct kernels run; for the split layouts, whose code and scale
-// bytes already leave each store instruction contiguous, staging measured
-// no faster).
-int32_t staged_span(const KvLayout& L, int32_t num_heads, int32_t head_size) {
-    const int64_t dr = head_size / 2, fd = dr + head_size / 16, span = num_heads * fd;
+// The staged kernels apply when each (token, side) of the layout is at most
+// two contiguous, 16-byte aligned runs of at most kKvMaxSpan bytes in all:
+//   rows  : [data | scales] rows, head after head -- one run of H * full_dim;
+//   split : the heads' data back to back (head stride head_size / 2) and the
+//           heads' scales back to back (head stride head_size / 16), each
+//           run a whole number of 16-byte pieces -- the NHD split layout.
+// Otherwise (HND, padded heads, odd sizes) the direct kernels run.
+KvStage staged_layout(const KvLayout& L, int32_t num_heads, int32_t head_size) {
+    const int64_t dr = head_size / 2, sr = head_size / 16, fd = dr + sr, span = num_heads * fd;
+    KvStage st{0, 0, 0, 0, 0};
+    if (span > kKvMaxSpan || L.side_stride % 16 || L.block_stride % 16 || L.data_offset % 16 ||
+        L.data_token_stride % 16)
+        return st;
     const bool rows = L.data_head_stride == fd && L.scale_head_stride == fd && L.scale_offset == L.data_offset + dr &&
-                      L.data_token_stride == span && L.scale_token_stride == span;
-    const bool aligned = L.data_offset % 16 == 0 && span % 16 == 0 && L.side_stride % 16 == 0 &&
-                         L.block_stride % 16 == 0;
-    return rows && aligned && span <= kKvMaxSpan ? (int32_t)span : 0;
+                      L.data_token_stride == span && L.scale_token_stride == span && span % 16 == 0;
+    if (rows) return KvStage{(int32_t)span, (int32_t)span, (int32_t)fd, (int32_t)dr, (int32_t)fd};
+    const int64_t drun = num_heads * dr, srun = num_heads * sr;
+    const bool split = L.data_head_stride == dr && L.scale_head_stride == sr && drun % 16 == 0 && srun % 16 == 0 &&
+                       L.scale_offset % 16 == 0 && L.scale_token_stride % 16 == 0;
+    if (split) return KvStage{(int32_t)span, (int32_t)drun, (int32_t)dr, (int32_t)drun, (int32_t)sr};
+    return st;
 }
 
 }  // namespace gcache
