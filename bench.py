@@ -624,8 +624,10 @@ KERNEL_OPS = {
     "void gcache::k_write_nvfp4_ds_mla": "nvfp4_ds_mla_write",
     "void gcache::k_write_fp8_ds_mla": "fp8_ds_mla_write",
     "void gcache::k_gather_ds_mla<true>": "nvfp4_ds_mla_gather",
-    "void gcache::k_reshape_and_cache_nvfp4<false>": "nvfp4_kv_write",
+    "void gcache::k_reshape_and_cache_nvfp4<true>": "nvfp4_kv_write",      # staged (split or row layouts)
+    "void gcache::k_reshape_and_cache_nvfp4<false>": "nvfp4_kv_write",     # direct (other layouts)
     "void gcache::k_gather_ds_mla<false>": "fp8_ds_mla_gather",
+    "void gcache::k_gather_nvfp4_kv<true>": "nvfp4_kv_gather",
     "void gcache::k_gather_nvfp4_kv<false>": "nvfp4_kv_gather",
 }
 CALIBRATION_KERNEL = "CUDAFunctorOnSelf_add"

@@ -64,8 +64,13 @@ def test_kernel_names_map_to_ops():
         "nvfp4_ds_mla_gather"
     assert bench.kernel_op("void gcache::k_gather_ds_mla<false>(gcache::DsMlaGatherParams, long)") == \
         "fp8_ds_mla_gather"
-    assert bench.kernel_op("void gcache::k_gather_nvfp4_kv<true>(gcache::KvGatherParams, long)") is None
+    for staged in ("true", "false"):          # the staged and the direct per-head kernels are one op each
+        assert bench.kernel_op(f"void gcache::k_gather_nvfp4_kv<{staged}>(gcache::KvGatherParams, long)") == \
+            "nvfp4_kv_gather"
+        assert bench.kernel_op(f"void gcache::k_reshape_and_cache_nvfp4<{staged}>(gcache::KvWriteParams, long)") == \
+            "nvfp4_kv_write"
     assert bench.kernel_op("gcache::k_gather_bf16(gcache::DsMlaGatherParams, long)") is None
+    assert bench.kernel_op("void gcache::k_convert_req_index<true>(gcache::SparseIndexParams, long)") is None
 
 
 def test_more_than_one_gpu_is_refused():
