@@ -58,7 +58,8 @@ class KernelTimer:
             hip = ctypes.CDLL("libamdhip64.so.7", mode=os.RTLD_NOLOAD | os.RTLD_NOW)
             hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
             hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
-            hip.hipEventCreate.restype = hip.hipEventElapsedTime.restype = ctypes.c_int
+            hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            hip.hipEventCreate.restype = hip.hipEventElapsedTime.restype = hip.hipEventDestroy.restype = ctypes.c_int
             KernelTimer._hip = hip
 
     def _pair(self, i):
@@ -76,6 +77,13 @@ class KernelTimer:
 
     def arm(self, i):
         self.gc.time_next_launch(*self._pair(i))
+
+    def close(self):
+        """Destroy the events (after their last read)."""
+        for pair in self.ev.values():
+            for e in pair:
+                KernelTimer._hip.hipEventDestroy(e)
+        self.ev = {}
 
     def ms(self, i):
         import ctypes
@@ -281,6 +289,8 @@ def main():
             live[i].append(timers[k].ms(i))
     ms_per_step = wall * 1e3 / args.steps
     live_ms = {ops[i][0]: float(np.mean(v)) for i, v in live.items()}
+    for t in timers + [kt]:
+        t.close()
 
     kernels = {}
     for name, nbytes, units, _ in ops:

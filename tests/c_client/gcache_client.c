@@ -15,7 +15,9 @@
  *       DIR/block_table.bin (int32 [B,MAXB]), DIR/ws.bin and DIR/ss.bin
  *       (int32 [B]).  Fills a cache of NB blocks x BS entries with 0xA5,
  *       writes the tokens into it, gathers TOTAL rows back, and writes
- *       DIR/cache.bin and DIR/out.bin (uint16 [TOTAL,576]).
+ *       DIR/cache.bin and DIR/out.bin (uint16 [TOTAL,576]).  The gather's
+ *       own duration is taken with two events bound to that kernel
+ *       (gcache_time_next_launch) and printed as gather_kernel_ms=...
  *
  * Exit status: 0 on success, 1 on a usage or I/O error, 2 when a library or
  * HIP call fails (its status is printed first).
@@ -149,6 +151,8 @@ static int roundtrip_mode(int argc, char** argv) {
     void *h_kv, *h_pe, *h_sl, *h_bt, *h_ws, *h_ss, *h_cache, *h_out;
     void *kv, *pe, *sl, *bt, *ws, *ss, *cache, *out;
     hipStream_t stream;
+    hipEvent_t ev_start, ev_stop;
+    float gather_ms = 0.0f;
 
     if (argc != 10) {
         fprintf(stderr, "usage: gcache_client roundtrip FMT DIR T NB BS B MAXB TOTAL\n");
@@ -193,21 +197,33 @@ static int roundtrip_mode(int argc, char** argv) {
     HIP_OK(hipMalloc(&out, out_bytes ? out_bytes : 16));
     HIP_OK(hipMemsetAsync(cache, 0xA5, cache_bytes, stream));
     if (out_bytes) HIP_OK(hipMemsetAsync(out, 0x00, out_bytes, stream));
+    HIP_OK(hipEventCreate(&ev_start));
+    HIP_OK(hipEventCreate(&ev_stop));
 
     if (nvfp4) {
         GC_OK(gcache_cache_write_nvfp4_ds_mla(kv, pe, cache, (const int64_t*)sl, T, 512, 64, NB, (int32_t)BS,
                                               BS * eb, eb, stream));
+        GC_OK(gcache_time_next_launch(ev_start, ev_stop));
         GC_OK(gcache_cache_gather_upconvert_nvfp4_ds_mla(cache, out, TOTAL, 576, (const int32_t*)bt, MAXB,
                                                          (const int32_t*)ws, (const int32_t*)ss, (int32_t)B, NB,
                                                          (int32_t)BS, BS * eb, eb, stream));
     } else {
         GC_OK(gcache_cache_write_fp8_ds_mla(kv, pe, cache, (const int64_t*)sl, T, 512, 64, NB, (int32_t)BS,
                                             BS * eb, eb, stream));
+        GC_OK(gcache_time_next_launch(ev_start, ev_stop));
         GC_OK(gcache_cache_gather_upconvert_fp8_ds_mla(cache, out, TOTAL, 576, (const int32_t*)bt, MAXB,
                                                        (const int32_t*)ws, (const int32_t*)ss, (int32_t)B, NB,
                                                        (int32_t)BS, BS * eb, eb, stream));
     }
     HIP_OK(hipStreamSynchronize(stream));
+    if (TOTAL > 0) {                     /* the gather launched and consumed the hook */
+        HIP_OK(hipEventElapsedTime(&gather_ms, ev_start, ev_stop));
+        printf("gather_kernel_ms=%.6f\n", gather_ms);
+    } else {
+        GC_OK(gcache_time_next_launch(NULL, NULL));   /* nothing launched: disarm */
+    }
+    HIP_OK(hipEventDestroy(ev_start));
+    HIP_OK(hipEventDestroy(ev_stop));
 
     h_cache = malloc(cache_bytes);
     h_out = malloc(out_bytes ? out_bytes : 1);

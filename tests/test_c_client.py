@@ -114,3 +114,6 @@ def test_roundtrip_from_c(orc, tmp_path, fmt):
                       w.block_size)
         out = np.fromfile(d / "out.bin", np.uint16).reshape(g.total_tokens, 576)
         assert np.array_equal(out, ref), f"{fmt} {name}: gathered rows differ from the oracle"
+        # the gather's kernel-bound events (gcache_time_next_launch) recorded a duration
+        ms = [float(l.split("=", 1)[1]) for l in r.stdout.splitlines() if l.startswith("gather_kernel_ms=")]
+        assert len(ms) == (1 if g.total_tokens > 0 else 0) and all(0.0 < m < 1000.0 for m in ms), r.stdout
