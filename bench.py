@@ -99,7 +99,9 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    # ~60 ms of back-to-back steps: after an idle gap the first tens of
+    # milliseconds of work run measurably slower (clocks ramping back up).
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=40.0,
                     help="approximate CPU seconds for the oracle baseline sample")

@@ -73,6 +73,24 @@ __device__ __forceinline__ void store_staged(const DsMlaWriteParams& p, const ui
     }
 }
 
+// Slot ids of tokens t_first + STRIDE*i (-1 past the end or outside the
+// cache).  The loads are unconditional -- a token past the end reads the last
+// token's id and drops it -- so they are all in flight at once; behind a
+// bounds branch each would wait for the one before it (one more memory round
+// trip per token before the wave's input loads can start).
+template <int N, int STRIDE>
+__device__ __forceinline__ void load_slots(const DsMlaWriteParams& p, int64_t t_first, int64_t (&slot)[N]) {
+    int64_t raw[N];
+#pragma unroll
+    for (int i = 0; i < N; i++) {
+        const int64_t t = t_first + STRIDE * i;
+        raw[i] = p.slots[t < p.num_tokens ? t : p.num_tokens - 1];
+    }
+#pragma unroll
+    for (int i = 0; i < N; i++)
+        slot[i] = t_first + STRIDE * i < p.num_tokens ? valid_slot(raw[i], p.num_slots) : -1;
+}
+
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float v) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
@@ -96,11 +114,7 @@ __global__ __launch_bounds__(WAVES * kWave) void k_write_nvfp4_ds_mla(DsMlaWrite
 
     int64_t slot[kTokPerWave];                           // wave-uniform
     uint4 v[kTokPerWave];
-#pragma unroll
-    for (int i = 0; i < kTokPerWave; i++) {
-        const int64_t t = t0 + w + WAVES * i;
-        slot[i] = t < p.num_tokens ? valid_slot(p.slots[t], p.num_slots) : -1;
-    }
+    load_slots<kTokPerWave, WAVES>(p, t0 + w, slot);
 #pragma unroll
     for (int i = 0; i < kTokPerWave; i++)                // all loads first; padding reads nothing
         if (slot[i] >= 0)
@@ -176,11 +190,7 @@ __global__ __launch_bounds__(WAVES * kWave) void k_write_fp8_ds_mla(DsMlaWritePa
 
     int64_t slot[kTokPerWave];                           // wave-uniform
     uint4 v[kTokPerWave];
-#pragma unroll
-    for (int i = 0; i < kTokPerWave; i++) {
-        const int64_t t = t0 + w + WAVES * i;
-        slot[i] = t < p.num_tokens ? valid_slot(p.slots[t], p.num_slots) : -1;
-    }
+    load_slots<kTokPerWave, WAVES>(p, t0 + w, slot);
 #pragma unroll
     for (int i = 0; i < kTokPerWave; i++)
         if (slot[i] >= 0)
