@@ -394,6 +394,26 @@ def device_ms(torch, fn, steps, spin_cycles=300_000):
     return float(np.mean([a.elapsed_time(b) for a, b in ev]))
 
 
+def kernel_ms(torch, gc, fn, steps, cold=False):
+    """Mean duration of the one library kernel that fn() launches, from HIP
+    events bound to that kernel's own begin and end (gcache_time_next_launch),
+    so no enqueue gap is counted (the figure rocprofv3 reports).  cold: each
+    launch follows a 2 GiB write that evicts L2 and the 256 MB MALL."""
+    fn()
+    flush = torch.empty(2 << 30, dtype=torch.uint8, device="cuda") if cold else None
+    timer = KernelTimer(gc)
+    for k in range(steps):
+        if cold:
+            flush.zero_()
+        timer.arm(k)
+        fn()
+    torch.cuda.synchronize()
+    ms = float(np.mean([timer.ms(k) for k in range(steps)]))
+    timer.close()
+    del flush
+    return ms
+
+
 def _extra(ms, nbytes, units, workload, **more):
     return {"ms": round(ms, 5), "bytes": nbytes, "units": units, **more,
             "GB_per_s": round(nbytes / (ms * 1e6), 1),
@@ -401,13 +421,16 @@ def _extra(ms, nbytes, units, workload, **more):
 
 
 def measure_extras(torch, gc, g3, steps, dev_arr, cache3, perhead):
-    """Outside the timed step, device times (see device_ms) of:
+    """Outside the timed step, kernel durations (kernel_ms: events bound to
+    the kernel's own begin and end) of:
     (1) the BF16 comparator gather (same walk, 1152-byte bf16 entries copied)
         over the nvfp4 prefill gather's requests and cache geometry -- what a
         walk-driven gather of full rows reaches on this device;
     (2) the chunked-context driver gathering every request's whole nvfp4
         context (the prefill requests' lengths, from position 0) through a
-        65536-row workspace, and the same pass's wall time on an idle GPU;
+        65536-row workspace (several launches and a metadata upload, so
+        device time between events around the pass, see device_ms), and the
+        same pass's wall time on an idle GPU;
     (3) the sparse index conversion, 4096 rows x top-2048;
     (4) the per-head workload under the split layout and under reading B
         (interleaved [data | scale] rows);
@@ -423,7 +446,7 @@ def measure_extras(torch, gc, g3, steps, dev_arr, cache3, perhead):
         .view(torch.bfloat16).reshape(nb, bs, 576).cuda()
     dst = torch.empty((g3.total_tokens, 576), dtype=torch.bfloat16, device="cuda")
     bt, ws, ss = dev_arr(g3.block_table), dev_arr(g3.workspace_starts), dev_arr(g3.seq_starts)
-    ms = device_ms(torch, lambda: gc.cache_gather_bf16(cache, dst, bt, ws, ss), steps)
+    ms = kernel_ms(torch, gc, lambda: gc.cache_gather_bf16(cache, dst, bt, ws, ss), steps)
     out["bf16_gather_comparator"] = _extra(
         ms, g3.total_tokens * 2 * 1152, g3.total_tokens,
         f"{g3.total_tokens} rows of the nvfp4 prefill gather over a bf16 cache {nb} x {bs} x 1152 B "
@@ -462,7 +485,7 @@ def measure_extras(torch, gc, g3, steps, dev_arr, cache3, perhead):
     req, idx, sbt, sbs, snb = synth.sparse_index_case()
     req_d, idx_d, sbt_d = dev_arr(req), dev_arr(idx), dev_arr(sbt)
     sout = torch.empty_like(idx_d)
-    ms = device_ms(torch, lambda: gc.convert_req_index_to_global_index(req_d, idx_d, sbt_d, sbs, snb, out=sout),
+    ms = kernel_ms(torch, gc, lambda: gc.convert_req_index_to_global_index(req_d, idx_d, sbt_d, sbs, snb, out=sout),
                    steps)
     out["sparse_index_conversion"] = _extra(
         ms, idx.size * 8 + req.size * 4, int(idx.size),
@@ -487,17 +510,17 @@ def measure_extras(torch, gc, g3, steps, dev_arr, cache3, perhead):
     for lname, L in layouts.items():
         what = ("the default split layout" if lname == "split_rows" else
                 f"each (token, head) cache row laid out as [{hs // 2} data | {hs // 16} scale] bytes")
-        ms = device_ms(torch, lambda: gc.reshape_and_cache_nvfp4(d["k5"], d["v5"], cache5, d["sl5"], d["ks5"],
-                                                                 d["vs5"], layout=L), steps)
+        ms = kernel_ms(torch, gc, lambda: gc.reshape_and_cache_nvfp4(d["k5"], d["v5"], cache5, d["sl5"], d["ks5"],
+                                                                     d["vs5"], layout=L), steps)
         out[f"perhead_write_{lname}"] = _extra(ms, kv_write_bytes(w5), w5.slot_mapping.shape[0],
                                                f"the per-head write workload, {what}")
-        ms = device_ms(torch, lambda: gc.gather_upconvert_nvfp4_kv(cache5, d["ko5"], d["vo5"], d["bt5"], d["ws5"],
-                                                                   d["ks5"], d["vs5"], seq_starts=d["ss5"],
-                                                                   layout=L), steps)
+        ms = kernel_ms(torch, gc, lambda: gc.gather_upconvert_nvfp4_kv(cache5, d["ko5"], d["vo5"], d["bt5"], d["ws5"],
+                                                                       d["ks5"], d["vs5"], seq_starts=d["ss5"],
+                                                                       layout=L), steps)
         out[f"perhead_gather_{lname}"] = _extra(ms, kv_gather_bytes(g5, H, hs), g5.total_tokens,
                                                 f"the per-head gather workload, {what}")
-        ms = device_ms(torch, lambda: gc.gather_upconvert_nvfp4_kv(cache5, ko_p, vo_p, bt_p, ws_p, d["ks5"], d["vs5"],
-                                                                   seq_starts=ss_p, layout=L), steps)
+        ms = kernel_ms(torch, gc, lambda: gc.gather_upconvert_nvfp4_kv(cache5, ko_p, vo_p, bt_p, ws_p, d["ks5"],
+                                                                       d["vs5"], seq_starts=ss_p, layout=L), steps)
         out[f"perhead_gather_prefill_walk_{lname}"] = _extra(
             ms, kv_gather_bytes(gp5, H, hs), gp5.total_tokens,
             f"per-head gather on a prefill walk: {len(gp5.workspace_starts)} requests, L ~ U[512, 6144] from "
@@ -520,11 +543,11 @@ def measure_extras(torch, gc, g3, steps, dev_arr, cache3, perhead):
               lambda: gc.gather_upconvert_nvfp4_kv(d["cache5"], d["ko5"], d["vo5"], d["bt5"], d["ws5"], d["ks5"],
                                                    d["vs5"], seq_starts=d["ss5"]),
               "the per-head gather workload, default split layout")]
-    cold = measure_cold(torch, [(n, b, u, fn) for n, b, u, fn, _ in small])
     for name, nbytes, units, fn, what in small:
-        warm = device_ms(torch, fn, steps)
+        warm = kernel_ms(torch, gc, fn, steps)
+        cold = kernel_ms(torch, gc, fn, steps, cold=True)
         out[name] = _extra(warm, nbytes, units, what + "; ms = warm (back to back), cold_ms = after evicting "
-                           "L2 and the MALL", cold_ms=cold[name]["ms"], cold_GB_per_s=cold[name]["GB_per_s"])
+                           "L2 and the MALL", cold_ms=round(cold, 5), cold_GB_per_s=round(nbytes / (cold * 1e6), 1))
     del cache2
     return out
 
@@ -760,7 +783,9 @@ def write_stats(prof_dir, bench_json, extras=False):
     if bench_json:
         b = json.load(open(bench_json))
         if extras:
-            md += ["", "Same-build HIP-event figures from `python bench.py --extras-only`:", "",
+            md += ["", "Same-build figures from an unprofiled `python bench.py --extras-only` run: kernel "
+                   "durations from HIP events bound to each kernel's own begin and end (gcache_time_next_launch), "
+                   "except the chunked-context pass (events around the whole pass of several launches):", "",
                    "| Extra | ms | GB/s | % of 8 TB/s |", "|---|---|---|---|"]
             for k, v in b["extras"].items():
                 md.append(f"| {k} | {v['ms']:.5f} | {v['GB_per_s']:.0f} | {100 * v['frac_of_hbm_peak']:.1f} |")
@@ -811,7 +836,7 @@ def decode_write_only(torch, gc, args):
     for name, eb, fn in (("decode_batch_nvfp4_write", NV, gc.cache_write_nvfp4_ds_mla),
                          ("decode_batch_fp8_write", F8, gc.cache_write_fp8_ds_mla)):
         cache = torch.zeros((w2.num_blocks, w2.block_size, eb), dtype=torch.uint8, device="cuda")
-        ms = device_ms(torch, lambda: fn(kv, pe, cache, sl), max(1, args.steps))
+        ms = kernel_ms(torch, gc, lambda: fn(kv, pe, cache, sl), max(1, args.steps))
         out[name] = _extra(ms, ds_write_bytes(w2, eb), w2.num_tokens,
                            f"{w2.num_tokens} decode tokens into {w2.num_blocks} x {w2.block_size} x {eb} B, "
                            f"{int((w2.slot_mapping < 0).sum())} padding slots")
@@ -864,8 +889,7 @@ def write_decode_traffic(fetch_dir, write_dir):
           "without replacement from all 65536, so most entries start inside a 128-byte line whose other "
           "bytes belong to entries this launch does not write. Counters are scaled as for the prefill pass "
           f"(fetch x{f_scale:.5f}, write x{w_scale:.5f}, from torch's elementwise add over 1 GiB in the same "
-          "run); each kernel: mean over its dispatches (one spin kernel and 20 launches each, plus the "
-          "first call).", "",
+          "run); each kernel: mean over its dispatches (20 launches each, plus the first call).", "",
           "| Kernel op | Dispatches | FETCH_SIZE (KiB, raw) | WRITE_SIZE (KiB, raw) | Read bytes (scaled) "
           "| Algorithmic read | Written bytes (scaled) | Entry bytes | Write ratio |",
           "|---|---|---|---|---|---|---|---|---|"]
