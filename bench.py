@@ -802,6 +802,24 @@ def write_stats(prof_dir, bench_json, extras=False):
                    f"({100 * b['roofline']['frac']:.1f} %); the metric's value (the pair's bytes over the pair's "
                    f"kernel time) {b['value']} GB/s, {100 * b['frac_of_hbm_peak']:.1f} % of 8 TB/s; whole six-op step "
                    f"{b['step_throughput']['value']} GB/s."]
+    traces = glob.glob(os.path.join(prof_dir, "*kernel_trace.csv"))
+    if not extras and traces:
+        # the profiled command runs 3 warm-up steps, 20 per-kernel-pass steps and 20 timed steps
+        trace = list(csv.DictReader(open(traces[0])))
+        phases = []
+        for op, prefix in (("nvfp4_ds_mla write", "void gcache::k_write_nvfp4_ds_mla"),
+                           ("nvfp4_ds_mla gather", "void gcache::k_gather_ds_mla<true>")):
+            ds = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in trace
+                        if r["Kernel_Name"].startswith(prefix))
+            if len(ds) == 43:
+                us = [(e - st) / 1e3 for st, e in ds]
+                phases.append(f"{op} {np.mean(us[:3]):.2f} / {np.mean(us[3:23]):.2f} / {np.mean(us[23:]):.2f} µs")
+        if phases:
+            md += ["", "rocprofv3's own durations of the metric's two kernels by phase of the profiled run "
+                   "(its kernel trace; warm-up / per-kernel pass / timed steps): " + "; ".join(phases) + ". "
+                   "The profiler times every dispatch; inside the timed steps bench.py binds events to these "
+                   "two kernels only, and those durations read a few per cent longer than the profiler's "
+                   "(a kernel after an unarmed neighbour carries part of that neighbour's tail)."]
     name = "extras_kernels_stats.md" if extras else "prefill_pass_all_kernels_stats.md"
     with open(os.path.join(ROOT, "profiles", name), "w") as f:
         f.write("\n".join(md) + "\n")
