@@ -4,6 +4,8 @@ every cache byte (sentinel-filled, so untouched bytes are checked too) and
 every bf16 output bit.  Sizes span several workgroups and ragged tails; the
 full-size workloads run in the launch configuration the benchmark times.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -906,6 +908,13 @@ def _random_ds_case(rng):
                 dst_extra=int(rng.choice([0, 8])), seed=int(rng.integers(1 << 30)))
 
 
+def _extra_sweep_seeds():
+    """GCACHE_SWEEP_SEEDS=N adds N more master seeds to each randomized sweep
+    (0 by default; 150 ran bit-exact: 28,800 DS-MLA and 7,200 per-head
+    cases on top of the default ones)."""
+    return range(int(os.environ.get("GCACHE_SWEEP_SEEDS", "0")))
+
+
 @pytest.mark.parametrize("fmt", ["nvfp4", "fp8"])
 def test_randomized_ds_sweep(g, orc, fmt):
     """96 seeded random cases per format: block sizes 1..128 (power-of-two
@@ -914,11 +923,18 @@ def test_randomized_ds_sweep(g, orc, fmt):
     with random lengths, empty requests, seq_starts and shared blocks, and a
     wider dst row -- every cache byte and every output bit against the
     oracle."""
+    seeds = [4242 if fmt == "nvfp4" else 4343]
+    seeds += [100000 + 2 * k + (fmt == "fp8") for k in _extra_sweep_seeds()]
+    for seed in seeds:
+        _ds_sweep(g, orc, fmt, seed)
+
+
+def _ds_sweep(g, orc, fmt, master_seed):
     eb = NV if fmt == "nvfp4" else F8
-    master = np.random.default_rng(4242 if fmt == "nvfp4" else 4343)
+    master = np.random.default_rng(master_seed)
     for n in range(96):
         c = _random_ds_case(master)
-        print(f"random DS case {fmt} #{n}: {c}", flush=True)
+        print(f"random DS case {fmt} master {master_seed} #{n}: {c}", flush=True)
         rng = np.random.default_rng(c["seed"])
         bs, nb, T = c["bs"], c["nb"], c["T"]
         estr = eb + 16 * c["ek"]
@@ -955,7 +971,12 @@ def test_randomized_perhead_sweep(g, orc):
     [data | scale] rows per (token, head) (staged kernels whenever a token's
     run is 16-byte aligned and at most 2048 bytes), 0..300 tokens with
     padding, gathered back per token -- every byte and bit."""
-    master = np.random.default_rng(4444)
+    for seed in [4444] + [200000 + k for k in _extra_sweep_seeds()]:
+        _perhead_sweep(g, orc, seed)
+
+
+def _perhead_sweep(g, orc, master_seed):
+    master = np.random.default_rng(master_seed)
     for n in range(48):
         H = int(master.integers(1, 10))
         hs = int(master.choice([16, 32, 48, 64, 80, 128, 256]))
@@ -967,7 +988,8 @@ def test_randomized_perhead_sweep(g, orc):
         if layout == "rows" and hs % 128:
             hs = 128                    # [data | scale] rows keep 8-byte data alignment only at hs % 128 == 0
         seed = int(master.integers(1 << 30))
-        print(f"random per-head case #{n}: H={H} hs={hs} bs={bs} nb={nb} T={T} pad={pad} layout={layout}",
+        print(f"random per-head case master {master_seed} #{n}: H={H} hs={hs} bs={bs} nb={nb} T={T} "
+              f"pad={pad} layout={layout}",
               flush=True)
         rng = np.random.default_rng(seed)
         if T == 0:
