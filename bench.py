@@ -308,6 +308,7 @@ def main():
         mix = {"nvfp4_ds_mla_write": (w3.num_tokens, 1152, NV), "fp8_ds_mla_write": (w4.num_tokens, 1152, F8),
                "nvfp4_ds_mla_gather": (g3.total_tokens, NV, 1152), "fp8_ds_mla_gather": (g4.total_tokens, F8, 1152)}
         extras["same_mix_ceilings"] = measure_ceilings(torch, [o for o in ops if o[0] in mix], mix)
+        extras["empty_grid_floor_us"] = measure_launch_floor(torch, gc)
         extras["gather_streaming_rate"] = measure_gather_streaming(torch, gc, [
             ("nvfp4_ds_mla_gather", g3.total_tokens, NV,
              lambda n: gc.cache_gather_upconvert_nvfp4_ds_mla(d["cache3"], d["dst3"][:n], d["bt3"], d["ws3"],
@@ -549,6 +550,37 @@ def measure_extras(torch, gc, g3, steps, dev_arr, cache3, perhead):
         out[name] = _extra(warm, nbytes, units, what + "; ms = warm (back to back), cold_ms = after evicting "
                            "L2 and the MALL", cold_ms=round(cold, 5), cold_GB_per_s=round(nbytes / (cold * 1e6), 1))
     del cache2
+    return out
+
+
+def measure_launch_floor(torch, gc, reps=21):
+    """Median duration between kernel-bound events of launches whose waves
+    exit without touching memory (gcache_bench_empty_grid in
+    libgcache_bench.so), for grids of 1 to 262144 workgroups: the cost any
+    kernel of that grid pays before and after its work.  The cache kernels'
+    grids: nvfp4 write 262144 x 64 lanes, fp8 write 262144 x 128, DS-MLA
+    gathers 10111 / 13705 x 256, per-head ops about 2048 x 256."""
+    import ctypes
+    from gather_concat_cache_amd import build
+    lib = ctypes.CDLL(build.BENCH_LIB)
+    fn = lib.gcache_bench_empty_grid
+    fn.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    fn.restype = ctypes.c_int
+    stream = torch.cuda.current_stream().cuda_stream
+    timer = KernelTimer(gc)
+    out = {}
+    for threads in (64, 128, 256):
+        for groups in (1, 2048, 10111, 40444, 262144):
+            t = []
+            for k in range(reps):
+                a, b = timer._pair(k)
+                rc = fn(groups, threads, a, b, stream)
+                if rc != 0:
+                    raise RuntimeError(f"gcache_bench_empty_grid returned {rc}")
+            torch.cuda.synchronize()
+            t = [timer.ms(k) for k in range(reps)]
+            out[f"{groups}x{threads}"] = round(float(np.median(t)) * 1e3, 2)
+    timer.close()
     return out
 
 

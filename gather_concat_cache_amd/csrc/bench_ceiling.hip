@@ -1,6 +1,8 @@
 // bench_ceiling.hip -- libgcache_bench.so: the same-mix copy that bench.py
 // uses as an on-device ceiling for the cache operations (declared in
 // include/gcache_bench.h).  Not part of the cache path.
+#include <hip/hip_ext.h>
+
 #include "../../include/gcache_bench.h"
 #include "gcache_device.h"
 
@@ -58,6 +60,12 @@ __global__ __launch_bounds__(1024) void k_copy_mix(CopyMixParams p, int64_t g0) 
     }
 }
 
+// No wave touches memory: the store is behind a condition no workgroup
+// meets (blockIdx.x never reaches 2^31), so the kernel is not empty code.
+__global__ __launch_bounds__(1024) void k_empty(int* never) {
+    if (blockIdx.x == 0x80000000u && threadIdx.x == 0) *never = 0;
+}
+
 }  // namespace
 
 extern "C" int gcache_bench_copy_mix(const void* src, void* dst, int64_t rows, int32_t read_bytes,
@@ -85,4 +93,14 @@ extern "C" int gcache_bench_copy_mix(const void* src, void* dst, int64_t rows, i
             return -6;
     }
     return 0;
+}
+
+extern "C" int gcache_bench_empty_grid(int64_t groups, int32_t threads, hipEvent_t start, hipEvent_t stop,
+                                       hipStream_t stream) {
+    if (groups < 1 || groups >= (int64_t(1) << 31) || threads < 64 || threads > 1024 || threads % 64)
+        return -2;
+    int* never = nullptr;
+    void* args[] = {&never};
+    return hipExtLaunchKernel(reinterpret_cast<const void*>(k_empty), dim3((unsigned)groups), dim3(threads), args,
+                              0, stream, start, stop, 0) == hipSuccess ? 0 : -6;
 }

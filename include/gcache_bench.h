@@ -39,6 +39,19 @@ int gcache_bench_copy_mix(const void* src, void* dst, int64_t rows, int32_t read
                           int32_t write_bytes, int32_t rows_per_group, int32_t threads,
                           hipStream_t stream);
 
+/*
+ * Launch cost floor: one launch of `groups` workgroups of `threads` lanes
+ * whose waves exit without touching memory, with `start` / `stop` (HIP
+ * events created by the caller, or NULL) bound to the kernel's own begin and
+ * end as for the cache entry points' timing hook, so the elapsed time between
+ * them is what any kernel of that grid pays before and after its work.
+ *  groups in [1, 2^31), threads a multiple of 64 in [64, 1024]
+ * Returns 0, -2 for a grid out of range, -6 when the launch fails.  Enqueued
+ * on `stream`; nothing is allocated or synchronized.
+ */
+int gcache_bench_empty_grid(int64_t groups, int32_t threads, hipEvent_t start, hipEvent_t stop,
+                            hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -178,7 +178,8 @@ def test_bench_helper_library():
     if not os.path.exists(build.BENCH_LIB):
         build.build()
     text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "gcache_bench.h")).read(), flags=re.S)
-    assert sorted(set(re.findall(r"\b(gcache_[a-z0-9_]+)\s*\(", text))) == ["gcache_bench_copy_mix"]
+    assert sorted(set(re.findall(r"\b(gcache_[a-z0-9_]+)\s*\(", text))) == ["gcache_bench_copy_mix",
+                                                                           "gcache_bench_empty_grid"]
     blib = C.CDLL(build.BENCH_LIB)
     f = blib.gcache_bench_copy_mix
     f.argtypes = [C.c_void_p, C.c_void_p, C.c_int64, C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_void_p]
@@ -192,3 +193,8 @@ def test_bench_helper_library():
     assert f(A16, A16, 10, 352, 1152, 16, 96, None) == -2            # not a whole number of waves
     assert f(A16, A16, 10, 1152, 352, 17, 1024, None) == -2          # more than 18 KiB staged
     assert f(A16 + 8, A16, 10, 352, 1152, 16, 256, None) == -3
+    e = blib.gcache_bench_empty_grid
+    e.argtypes = [C.c_int64, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p]
+    e.restype = C.c_int
+    for groups, threads in ((0, 256), (1 << 31, 256), (1, 0), (1, 96), (1, 1088)):
+        assert e(groups, threads, None, None, None) == -2
